@@ -1,0 +1,249 @@
+"""Benchmark of the SMOE routed-expert MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--copies C]
+
+A step is one full forward of the layer (route, group, gate/up + SwiGLU, down,
+combine; a stack of layers for the stacked workload) on synthetic inputs that
+are resident in HBM before timing starts. Expert banks are replicated into C
+distinct copies and consecutive steps rotate through them (and through
+distinct router logits), so the working set of the timed loop is far larger
+than the 256 MB Infinity Cache and every step reads its experts from HBM.
+
+Prints one JSON line (metric, value = tokens/s, roofline of the dominant
+kernel, CPU-oracle baseline on a bounded sample).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (% of peak), Qwen3-235B-shape Q4"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="qwen235b_q4_b1")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="distinct expert-bank copies to rotate through (0 = auto)")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=2)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+              "sharding is described in the design notes but not implemented", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synth
+    import quantised_moe_expert_amd as smoe
+
+    W = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    s_handle = stream.cuda_stream
+    lay = smoe.smoe_expert_layout_of(W.d_model, W.ffn_dim, W.bits, smoe.SMOE_SCALE_F32)
+    stride = lay.padded_size
+    raw = lay.raw_size
+    stack = W.n_layers > 1
+    copies = args.copies or (W.n_layers if stack else (16 if W.n_tokens == 1 else 8))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def make_bank(E, ffn, layout, stride_):
+        """E experts at `stride_`: uniform code bytes, lognormal fp32 scales,
+        zero padding; offsets from the library's layout query."""
+        bank = torch.randint(0, 256, (E, stride_), dtype=torch.uint8, device=dev, generator=gen)
+        for t in (layout.gate, layout.up, layout.down):
+            sc = bank[:, t.scales_offset: t.scales_offset + t.scales_bytes].view(torch.float32)
+            sc.copy_(torch.empty(sc.shape, device=dev).log_normal_(
+                math.log(0.02), 0.5, generator=gen))
+        bank[:, layout.raw_size:] = 0
+        return bank
+
+    banks, handles = [], []
+    shared_blobs = []
+    for c in range(copies):
+        bank = make_bank(W.num_experts, W.ffn_dim, lay, stride)
+        sh = None
+        sh_bytes = 0
+        if W.shared_ffn_dim:
+            sl = smoe.smoe_expert_layout_of(W.d_model, W.shared_ffn_dim, W.bits,
+                                            smoe.SMOE_SCALE_F32)
+            sh = make_bank(1, W.shared_ffn_dim, sl, sl.padded_size).reshape(-1)
+            sh_bytes = sh.numel()
+            shared_blobs.append(sh)
+        desc = smoe.make_desc(W.d_model, W.ffn_dim, W.num_experts, W.bits, stride,
+                              smoe.SMOE_SCALE_F32, W.shared_ffn_dim)
+        handles.append(smoe.smoe_load_blobs(desc, bank.data_ptr(), bank.numel(),
+                                            sh.data_ptr() if sh is not None else 0, sh_bytes))
+        banks.append(bank)
+    T, E, k = W.n_tokens, W.num_experts, W.top_k
+    n_logit_sets = 64
+    lg_sets = torch.randn((n_logit_sets, W.n_layers, T, E), device=dev, generator=gen)
+    if W.x_dtype == "bf16":
+        x = torch.randn((T, W.d_model), device=dev, generator=gen).to(torch.bfloat16)
+        x_dt = smoe.SMOE_DTYPE_BF16
+    else:
+        x = torch.randn((T, W.d_model), device=dev, generator=gen)
+        x_dt = smoe.SMOE_DTYPE_F32
+    h_state = torch.randn((T, W.d_model), device=dev, generator=gen) if stack else None
+    out = torch.empty((T, W.d_model), dtype=torch.float32, device=dev)
+    nws = smoe.smoe_workspace_bytes(handles[0], T, k)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    # unique experts each step reads (algorithmic bytes)
+    top = torch.topk(lg_sets, k, dim=-1).indices  # [S, L, T, k]
+    uniq = []
+    for s in range(n_logit_sets):
+        uniq.append(sum(int(torch.unique(top[s, l]).numel()) for l in range(W.n_layers)))
+    shared_raw = 0
+    if W.shared_ffn_dim:
+        shared_raw = smoe.smoe_expert_layout_of(W.d_model, W.shared_ffn_dim, W.bits,
+                                                smoe.SMOE_SCALE_F32).raw_size
+    act_bytes = W.n_layers * (T * W.d_model * (2 if W.x_dtype == "bf16" else 4)
+                              + T * E * 4 + T * W.d_model * 4)
+
+    def step(i):
+        c = i % copies
+        s = i % n_logit_sets
+        if stack:
+            smoe.smoe_decode_step(handles, h_state.data_ptr(), lg_sets[s].data_ptr(), T, k,
+                                  W.norm_topk_prob, 1e-6, ws.data_ptr(), nws, s_handle)
+        else:
+            smoe.smoe_moe_forward(handles[c], x.data_ptr(), x_dt, lg_sets[s, 0].data_ptr(), T, k,
+                                  W.norm_topk_prob, out.data_ptr(), 0, 0, ws.data_ptr(), nws,
+                                  s_handle)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if stack:
+        h_state.normal_(generator=gen)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tokens_per_s = T / (ms * 1e-3)
+    bytes_per_step = []
+    for i in range(args.steps):
+        s = (args.warmup + i) % n_logit_sets
+        bytes_per_step.append(uniq[s] * raw + W.n_layers * shared_raw + act_bytes)
+    alg_bytes = sum(bytes_per_step) / len(bytes_per_step)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    pairs = T * k * W.n_layers
+    avg_unique = sum(uniq[(args.warmup + i) % n_logit_sets] for i in range(args.steps)) / args.steps
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": W.name, "d_model": W.d_model, "ffn_dim": W.ffn_dim,
+            "num_experts": E, "top_k": k, "n_tokens": T, "bits": W.bits,
+            "group_size": 64, "scale_dtype": "f32", "x_dtype": W.x_dtype,
+            "norm_topk_prob": W.norm_topk_prob, "shared_ffn_dim": W.shared_ffn_dim,
+            "n_layers": W.n_layers, "bank_copies_rotated": copies,
+        },
+        "hbm_GBps": round(achieved, 1),
+        "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "expert_reads_per_s": round(avg_unique / (ms * 1e-3), 1),
+        "pairs_per_s": round(pairs / (ms * 1e-3), 1),
+        "wall_s_timed": round(t_wall, 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "whole forward (route, gate/up, down, combine launches)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_step": int(alg_bytes),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, W, banks[0], stride, lg_sets[0, 0], x,
+                                              shared_blobs[0] if shared_blobs else None)
+    print(json.dumps(result), flush=True)
+    for h in handles:
+        smoe.smoe_free(h)
+
+
+def cpu_baseline(args, W, bank, stride, logits, x, shared_blob):
+    """The oracle, as it stands, on host cores: repeated single-layer forwards
+    of the same workload (tokens of the first logit set, first bank copy) for
+    about --cpu-baseline-seconds."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_info
+
+    lg = logits.float().cpu().numpy()
+    xs = x.float().cpu().numpy()
+    T, k = W.n_tokens, W.top_k
+    # only the selected experts are copied to the host
+    sel = sorted({e for t in range(T) for e in O.route(lg[t], k, W.norm_topk_prob)[0]})
+    blobs = {e: bank[e].cpu().numpy() for e in sel}
+    sh = shared_blob.cpu().numpy() if shared_blob is not None else None
+    layer = O.OracleLayer(W.d_model, W.ffn_dim, W.num_experts, W.bits, None, stride,
+                          "f32", W.shared_ffn_dim, sh, expert_blobs=blobs)
+    t0 = time.perf_counter()
+    n_tok = 0
+    reps = 0
+    while True:
+        layer.drop_cache()
+        for t in range(T):
+            O.moe_forward(layer, xs[t:t + 1], lg[t:t + 1], k, W.norm_topk_prob)
+            n_tok += 1
+            if time.perf_counter() - t0 > args.cpu_baseline_seconds:
+                break
+        reps += 1
+        if time.perf_counter() - t0 > args.cpu_baseline_seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": round(n_tok / dt, 4),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{n_tok} token forwards of one {W.name} layer (experts dequantised "
+                   f"from the blob bytes per forward), {dt:.1f} s, "
+                   f"host cpu_count={os.cpu_count()}"),
+    }
+
+
+if __name__ == "__main__":
+    main()

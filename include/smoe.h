@@ -1,0 +1,202 @@
+/*
+ * smoe.h -- C ABI of the MI355X (gfx950) SMOE routed-expert MoE FFN library.
+ *
+ * The library computes one MoE feed-forward layer whose routed experts are
+ * stored as SMOE-Q4 or SMOE-Q2 group-64 symmetric-quantised weights in the
+ * .smoe expert-blob layout, and (optionally) a stack of such layers with an
+ * RMSNorm + residual around each.
+ *
+ * Sources the operations follow (page title, section):
+ *  - ".smoe Binary Format", "Expert Blob Architecture": one blob per expert,
+ *    [gate codes][gate scales][up codes][up scales][down codes][down scales]
+ *    then zero padding to a 16,384-byte boundary; codes take
+ *    ceil(rows*cols*bits/8) bytes, scales one value per 64 weights of the
+ *    flattened [rows, cols] tensor; "Tensor Descriptor": gate and up are
+ *    [ffn_dim, d_model], down is [d_model, ffn_dim] (the weights' original
+ *    [out, in] shapes); "Immutable Encoding": little-endian.
+ *  - "SMOE Quantisation", "Quantisation Levels", "Bit Packing", "Decoding:
+ *    Metal Kernel": codes packed least-significant-bits first (2 per byte for
+ *    Q4, 4 per byte for Q2); weight = (code - m) / m * scale with m = 7.5
+ *    (Q4) or 1.5 (Q2).
+ *  - "CMF v2 Format Specification", section 2.2 "MoE": softmax over all router
+ *    logits, top-k with ties broken toward the lower expert index, optional
+ *    renormalisation of the k selected probabilities, weighted sum of the
+ *    selected experts' SwiGLU outputs, and an always-on shared expert added
+ *    with weight 1.
+ *  - "Model Agnosticism", "Expanding the Frontier": SiLU/SwiGLU experts only,
+ *    at most 16 routed experts per token.
+ *  - ".smoe Binary Format", "Arch Block": RMS-norm epsilon 1e-6.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named d_* are device pointers (HIP device memory on the current
+ *    device). The caller allocates, owns and frees all of them; the library
+ *    only borrows them for the duration of the call (or, for the blob bank
+ *    given to smoe_load_blobs, until smoe_free).
+ *  - hip_stream is a hipStream_t (NULL = the legacy default stream). All GPU
+ *    work of a call is enqueued on it; calls return without synchronising.
+ *  - Return value: SMOE_OK (0) or a negative SMOE_E_* code. On failure a
+ *    message is available from smoe_last_error() (thread-local, valid until
+ *    the next call on the same thread). Argument checks happen on the host
+ *    before anything is enqueued, so a failed call enqueues no GPU work
+ *    unless it returns SMOE_E_HIP. No C++ exception crosses this ABI.
+ *  - Device faults caused by pointers that do not satisfy the stated sizes
+ *    cannot be detected by the library; they surface on the caller's next
+ *    synchronisation.
+ */
+#ifndef SMOE_H_
+#define SMOE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMOE_ABI_VERSION 1
+
+/* Status codes. */
+#define SMOE_OK 0
+#define SMOE_E_ARG (-1)         /* null pointer, value out of range, bad flag     */
+#define SMOE_E_LAYOUT (-2)      /* blob bank too small, misaligned, bad stride    */
+#define SMOE_E_UNSUPPORTED (-3) /* valid for the format, not built in this library */
+#define SMOE_E_HIP (-4)         /* a HIP runtime call failed (launch, attributes) */
+#define SMOE_E_WORKSPACE (-5)   /* workspace null or smaller than required        */
+
+/* Activation dtypes. */
+#define SMOE_DTYPE_F32 0
+#define SMOE_DTYPE_BF16 1
+
+/* Scale storage dtypes. The .smoe files store fp16 scales; fp32 is accepted
+ * as well (same layout, 4-byte scales). */
+#define SMOE_SCALE_F32 0
+#define SMOE_SCALE_F16 1
+
+/* Limits of this build. */
+#define SMOE_GROUP_SIZE 64       /* the only quantisation group size          */
+#define SMOE_BLOB_ALIGN 16384    /* blob stride granularity                   */
+#define SMOE_MAX_TOP_K 16        /* routing width cap                         */
+#define SMOE_MAX_EXPERTS 512     /* routed experts per layer                  */
+#define SMOE_MAX_TOKENS 1024     /* tokens per smoe_moe_forward call          */
+#define SMOE_BANK_ALIGN 256      /* required alignment of blob base pointers  */
+
+/* Description of one MoE layer's expert bank. */
+typedef struct smoe_layer_desc {
+  uint32_t d_model;        /* hidden size; multiple of 64                       */
+  uint32_t ffn_dim;        /* routed expert intermediate size; multiple of 64  */
+  uint32_t num_experts;    /* routed experts E, 1..SMOE_MAX_EXPERTS            */
+  uint32_t bits;           /* 4 (SMOE-Q4) or 2 (SMOE-Q2)                       */
+  uint32_t group_size;     /* must be 64                                        */
+  uint32_t scale_dtype;    /* SMOE_SCALE_F32 or SMOE_SCALE_F16                  */
+  uint64_t blob_stride;    /* bytes from expert e's blob to e+1's; a multiple
+                              of 16,384 and >= the raw blob size               */
+  uint32_t shared_ffn_dim; /* 0 = no shared expert, else its ffn (multiple of 64) */
+  uint32_t reserved;       /* must be 0                                         */
+} smoe_layer_desc;
+
+/* Byte layout of one tensor inside an expert blob. */
+typedef struct smoe_tensor_layout {
+  uint64_t codes_offset;   /* from the start of the blob */
+  uint64_t codes_bytes;    /* ceil(rows*cols*bits/8)     */
+  uint64_t scales_offset;
+  uint64_t scales_bytes;   /* ceil(rows*cols/64) * scale size */
+  uint32_t rows, cols;
+} smoe_tensor_layout;
+
+/* Byte layout of one expert blob. */
+typedef struct smoe_expert_layout {
+  smoe_tensor_layout gate, up, down;
+  uint64_t raw_size;       /* end of the down scales                   */
+  uint64_t padded_size;    /* raw_size rounded up to 16,384 bytes      */
+} smoe_expert_layout;
+
+/* Opaque handle: host-side metadata of a layer. Holds no device memory. */
+typedef struct smoe_layer smoe_layer;
+
+/* Library version (SMOE_ABI_VERSION). */
+int smoe_version(void);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* smoe_last_error(void);
+
+/* Host-only: byte layout of one expert blob of the given shape
+ * (".smoe Binary Format", Expert Blob Architecture). Fills *out.
+ * Errors: SMOE_E_ARG for a null out, bits not in {2,4}, a zero or
+ * non-multiple-of-64 dimension, or an unknown scale dtype. */
+int smoe_expert_layout_of(uint32_t d_model, uint32_t ffn_dim, uint32_t bits,
+                          uint32_t scale_dtype, smoe_expert_layout* out);
+
+/* Register a resident expert bank (and optional shared-expert blob).
+ *  desc          layer description (copied).
+ *  d_blobs       device pointer to E blobs, expert e at d_blobs + e*blob_stride;
+ *                SMOE_BANK_ALIGN-aligned. Borrowed until smoe_free.
+ *  nbytes        size of the bank; must be >= (E-1)*blob_stride + raw_size.
+ *  d_shared_blob device pointer to one blob of shape (d_model, shared_ffn_dim)
+ *                in the same layout, or NULL when shared_ffn_dim == 0.
+ *  shared_nbytes its size (>= its raw size).
+ *  out           receives the handle (NULL on failure).
+ * No GPU work, no device allocation. Errors: SMOE_E_ARG (bad desc fields or
+ * null pointers), SMOE_E_LAYOUT (stride, size or alignment), SMOE_E_UNSUPPORTED
+ * (a tensor width this build has no kernel for). */
+int smoe_load_blobs(const smoe_layer_desc* desc, const void* d_blobs, uint64_t nbytes,
+                    const void* d_shared_blob, uint64_t shared_nbytes, smoe_layer** out);
+
+/* Release a handle (NULL is allowed). Does not touch the borrowed memory. */
+void smoe_free(smoe_layer* layer);
+
+/* Bytes of device workspace smoe_moe_forward needs for n_tokens tokens and
+ * top_k (0 on invalid arguments). smoe_decode_step needs the same amount for
+ * the largest layer it runs. */
+uint64_t smoe_workspace_bytes(const smoe_layer* layer, int n_tokens, int top_k);
+
+/* Routing only ("CMF v2 Format Specification", 2.2):
+ *  d_logits  [n_tokens, n_experts] fp32, row-major.
+ *  d_ids     [n_tokens, top_k] int32 out: expert ids by descending logit,
+ *            equal logits in ascending id.
+ *  d_weights [n_tokens, top_k] fp32 out: softmax-over-all probability of each
+ *            selected expert, renormalised to sum 1 when norm_topk_prob != 0.
+ * Errors: SMOE_E_ARG (nulls, n_tokens < 0 or > SMOE_MAX_TOKENS, n_experts
+ * outside 1..SMOE_MAX_EXPERTS, top_k outside 1..min(16, n_experts)),
+ * SMOE_E_HIP. n_tokens == 0 is a no-op. Non-finite logits give unspecified
+ * (but in-bounds) ids. */
+int smoe_route(const float* d_logits, int n_tokens, int n_experts, int top_k,
+               int norm_topk_prob, int32_t* d_ids, float* d_weights, void* hip_stream);
+
+/* One MoE layer forward:
+ *   out[t] = sum_j w[t,j] * down_e(silu(gate_e x[t]) * up_e x[t])   (e = ids[t,j])
+ *            + shared(x[t])                                         (if present)
+ *  d_x        [n_tokens, d_model], dtype x_dtype (SMOE_DTYPE_BF16 or _F32),
+ *             16-byte aligned, row-major.
+ *  d_logits   [n_tokens, num_experts] fp32 router logits.
+ *  d_out      [n_tokens, d_model] fp32 out (overwritten).
+ *  d_topk_ids, d_topk_w  optional [n_tokens, top_k] copies of the routing
+ *             result (NULL to skip).
+ *  d_workspace at least smoe_workspace_bytes(layer, n_tokens, top_k) bytes,
+ *             256-byte aligned; contents are scratch and need no clearing.
+ * Tokens that share an expert read its weights once per call.
+ * Errors: SMOE_E_ARG, SMOE_E_WORKSPACE, SMOE_E_HIP. n_tokens == 0 is a no-op.
+ * Activations must be finite with |x| < 2^100 (they are rescaled by a power
+ * of two per vector before the fp16 dot products). */
+int smoe_moe_forward(const smoe_layer* layer, const void* d_x, int x_dtype,
+                     const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
+                     float* d_out, int32_t* d_topk_ids, float* d_topk_w,
+                     void* d_workspace, uint64_t ws_bytes, void* hip_stream);
+
+/* Stacked decode step over n_layers MoE layers (same d_model):
+ *   for l in 0..n_layers-1:  h = h + MoE_l(rms_norm(h, eps))
+ * with unit-gain RMSNorm n = h / sqrt(mean(h^2) + eps) per token.
+ *  layers     array of n_layers handles.
+ *  d_h        [n_tokens, d_model] fp32, updated in place (the residual stream).
+ *  d_logits   [n_layers, n_tokens, num_experts] fp32, one routing per layer.
+ *  eps        RMSNorm epsilon (the pages' kernels use 1e-6).
+ *  d_workspace, ws_bytes  as for smoe_moe_forward, sized for the largest layer.
+ * Errors as smoe_moe_forward, plus SMOE_E_ARG for n_layers < 1, mismatched
+ * d_model, or eps <= 0. */
+int smoe_decode_step(const smoe_layer* const* layers, int n_layers, float* d_h,
+                     const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
+                     float eps, void* d_workspace, uint64_t ws_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMOE_H_ */

@@ -1,0 +1,201 @@
+"""ctypes binding of the SMOE C ABI (include/smoe.h).
+
+Argument marshalling only: every function forwards to the function of the
+same name in ``libsmoe.so`` and turns a negative status into
+:class:`SmoeError`. Pointers are plain integers (device addresses, e.g. a
+torch tensor's ``data_ptr()``); streams are ``hipStream_t`` handles as
+integers (e.g. ``torch.cuda.current_stream().cuda_stream``), 0 for the null
+stream. The library is loaded on first use and a missing or stale build is a
+hard error: there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+LIB_NAME = "libsmoe.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+SMOE_OK = 0
+SMOE_E_ARG = -1
+SMOE_E_LAYOUT = -2
+SMOE_E_UNSUPPORTED = -3
+SMOE_E_HIP = -4
+SMOE_E_WORKSPACE = -5
+
+SMOE_DTYPE_F32 = 0
+SMOE_DTYPE_BF16 = 1
+SMOE_SCALE_F32 = 0
+SMOE_SCALE_F16 = 1
+
+SMOE_MAX_TOP_K = 16
+SMOE_MAX_EXPERTS = 512
+SMOE_MAX_TOKENS = 1024
+
+# every symbol include/smoe.h declares
+EXPORTED = (
+    "smoe_version", "smoe_last_error", "smoe_expert_layout_of", "smoe_load_blobs",
+    "smoe_free", "smoe_workspace_bytes", "smoe_route", "smoe_moe_forward",
+    "smoe_decode_step",
+)
+
+
+class SmoeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"smoe error {code}: {message}")
+        self.code = code
+
+
+class smoe_layer_desc(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_uint32),
+        ("ffn_dim", ctypes.c_uint32),
+        ("num_experts", ctypes.c_uint32),
+        ("bits", ctypes.c_uint32),
+        ("group_size", ctypes.c_uint32),
+        ("scale_dtype", ctypes.c_uint32),
+        ("blob_stride", ctypes.c_uint64),
+        ("shared_ffn_dim", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+class smoe_tensor_layout(ctypes.Structure):
+    _fields_ = [
+        ("codes_offset", ctypes.c_uint64),
+        ("codes_bytes", ctypes.c_uint64),
+        ("scales_offset", ctypes.c_uint64),
+        ("scales_bytes", ctypes.c_uint64),
+        ("rows", ctypes.c_uint32),
+        ("cols", ctypes.c_uint32),
+    ]
+
+
+class smoe_expert_layout(ctypes.Structure):
+    _fields_ = [
+        ("gate", smoe_tensor_layout),
+        ("up", smoe_tensor_layout),
+        ("down", smoe_tensor_layout),
+        ("raw_size", ctypes.c_uint64),
+        ("padded_size", ctypes.c_uint64),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_U32 = ctypes.c_uint32
+_U64 = ctypes.c_uint64
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libsmoe.so (built by __graft_entry__.build()); raises if absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            f"{p} is missing: build the HIP library first (python -c "
+            f"'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(p)
+    lib.smoe_version.restype = _I
+    lib.smoe_version.argtypes = []
+    lib.smoe_last_error.restype = ctypes.c_char_p
+    lib.smoe_last_error.argtypes = []
+    lib.smoe_expert_layout_of.restype = _I
+    lib.smoe_expert_layout_of.argtypes = [_U32, _U32, _U32, _U32,
+                                          ctypes.POINTER(smoe_expert_layout)]
+    lib.smoe_load_blobs.restype = _I
+    lib.smoe_load_blobs.argtypes = [ctypes.POINTER(smoe_layer_desc), _P, _U64, _P, _U64,
+                                    ctypes.POINTER(_P)]
+    lib.smoe_free.restype = None
+    lib.smoe_free.argtypes = [_P]
+    lib.smoe_workspace_bytes.restype = _U64
+    lib.smoe_workspace_bytes.argtypes = [_P, _I, _I]
+    lib.smoe_route.restype = _I
+    lib.smoe_route.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P]
+    lib.smoe_moe_forward.restype = _I
+    lib.smoe_moe_forward.argtypes = [_P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _U64, _P]
+    lib.smoe_decode_step.restype = _I
+    lib.smoe_decode_step.argtypes = [ctypes.POINTER(_P), _I, _P, _P, _I, _I, _I,
+                                     ctypes.c_float, _P, _U64, _P]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != SMOE_OK:
+        raise SmoeError(rc, smoe_last_error())
+
+
+def smoe_version() -> int:
+    return load_library().smoe_version()
+
+
+def smoe_last_error() -> str:
+    return load_library().smoe_last_error().decode()
+
+
+def smoe_expert_layout_of(d_model: int, ffn_dim: int, bits: int,
+                          scale_dtype: int = SMOE_SCALE_F32) -> smoe_expert_layout:
+    out = smoe_expert_layout()
+    _check(load_library().smoe_expert_layout_of(d_model, ffn_dim, bits, scale_dtype,
+                                                 ctypes.byref(out)))
+    return out
+
+
+def make_desc(d_model: int, ffn_dim: int, num_experts: int, bits: int,
+              blob_stride: int, scale_dtype: int = SMOE_SCALE_F32,
+              shared_ffn_dim: int = 0, group_size: int = 64) -> smoe_layer_desc:
+    return smoe_layer_desc(d_model, ffn_dim, num_experts, bits, group_size, scale_dtype,
+                           blob_stride, shared_ffn_dim, 0)
+
+
+def smoe_load_blobs(desc: smoe_layer_desc, d_blobs: int, nbytes: int,
+                    d_shared_blob: int = 0, shared_nbytes: int = 0) -> int:
+    """Returns the layer handle (an opaque integer)."""
+    h = _P()
+    _check(load_library().smoe_load_blobs(ctypes.byref(desc), d_blobs or None, nbytes,
+                                          d_shared_blob or None, shared_nbytes,
+                                          ctypes.byref(h)))
+    return h.value
+
+
+def smoe_free(layer: Optional[int]) -> None:
+    load_library().smoe_free(layer or None)
+
+
+def smoe_workspace_bytes(layer: int, n_tokens: int, top_k: int) -> int:
+    return load_library().smoe_workspace_bytes(layer, n_tokens, top_k)
+
+
+def smoe_route(d_logits: int, n_tokens: int, n_experts: int, top_k: int,
+               norm_topk_prob: bool, d_ids: int, d_weights: int, hip_stream: int = 0) -> None:
+    _check(load_library().smoe_route(d_logits or None, n_tokens, n_experts, top_k,
+                                     int(bool(norm_topk_prob)), d_ids or None,
+                                     d_weights or None, hip_stream or None))
+
+
+def smoe_moe_forward(layer: int, d_x: int, x_dtype: int, d_logits: int, n_tokens: int,
+                     top_k: int, norm_topk_prob: bool, d_out: int, d_topk_ids: int,
+                     d_topk_w: int, d_workspace: int, ws_bytes: int,
+                     hip_stream: int = 0) -> None:
+    _check(load_library().smoe_moe_forward(
+        layer, d_x or None, x_dtype, d_logits or None, n_tokens, top_k,
+        int(bool(norm_topk_prob)), d_out or None, d_topk_ids or None, d_topk_w or None,
+        d_workspace or None, ws_bytes, hip_stream or None))
+
+
+def smoe_decode_step(layers: Sequence[int], d_h: int, d_logits: int, n_tokens: int,
+                     top_k: int, norm_topk_prob: bool, eps: float, d_workspace: int,
+                     ws_bytes: int, hip_stream: int = 0) -> None:
+    arr = (_P * max(1, len(layers)))(*layers)
+    _check(load_library().smoe_decode_step(arr, len(layers), d_h or None, d_logits or None,
+                                           n_tokens, top_k, int(bool(norm_topk_prob)),
+                                           float(eps), d_workspace or None, ws_bytes,
+                                           hip_stream or None))

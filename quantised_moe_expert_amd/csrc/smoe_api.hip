@@ -1,0 +1,331 @@
+// Host side of the C ABI declared in include/smoe.h: argument validation,
+// layer handles, workspace layout and the per-call launch sequence.
+//
+// Nothing here allocates device memory: blobs, activations, outputs and the
+// workspace all belong to the caller.
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "smoe_internal.hpp"
+
+struct smoe_layer {
+  smoe::LayerInfo info;
+};
+
+namespace smoe {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SMOE_OK;
+}
+
+uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, uint64_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ".smoe Binary Format", Expert Blob Architecture: gate [ffn, d], up [ffn, d],
+// down [d, ffn]; codes ceil(n*bits/8) bytes then ceil(n/64) scales each.
+int layout_of(uint32_t d, uint32_t ffn, uint32_t bits, uint32_t sdt, smoe_expert_layout* L) {
+  if (!L) return fail(SMOE_E_ARG, "null layout output");
+  if (bits != 2 && bits != 4) return fail(SMOE_E_ARG, "bits must be 2 or 4 (got %u)", bits);
+  if (d == 0 || ffn == 0 || d % 64 || ffn % 64)
+    return fail(SMOE_E_ARG, "d_model (%u) and ffn_dim (%u) must be positive multiples of 64", d,
+                ffn);
+  if (sdt != SMOE_SCALE_F32 && sdt != SMOE_SCALE_F16)
+    return fail(SMOE_E_ARG, "unknown scale dtype %u", sdt);
+  const uint64_t ss = sdt == SMOE_SCALE_F32 ? 4 : 2;
+  uint64_t off = 0;
+  smoe_tensor_layout* t[3] = {&L->gate, &L->up, &L->down};
+  const uint32_t rows[3] = {ffn, ffn, d}, cols[3] = {d, d, ffn};
+  for (int i = 0; i < 3; ++i) {
+    const uint64_t n = (uint64_t)rows[i] * cols[i];
+    t[i]->rows = rows[i];
+    t[i]->cols = cols[i];
+    t[i]->codes_offset = off;
+    t[i]->codes_bytes = (n * bits + 7) / 8;
+    t[i]->scales_offset = off + t[i]->codes_bytes;
+    t[i]->scales_bytes = (n + 63) / 64 * ss;
+    off = t[i]->scales_offset + t[i]->scales_bytes;
+  }
+  L->raw_size = off;
+  L->padded_size = align_up(off, SMOE_BLOB_ALIGN);
+  return SMOE_OK;
+}
+
+int make_plan(uint32_t d, uint32_t ffn, uint32_t bits, uint32_t sdt, ExpertPlan* P,
+              smoe_expert_layout* Lout) {
+  smoe_expert_layout L;
+  int rc = layout_of(d, ffn, bits, sdt, &L);
+  if (rc) return rc;
+  P->d_model = (int)d;
+  P->ffn = (int)ffn;
+  P->raw_size = L.raw_size;
+  P->padded_size = L.padded_size;
+  const smoe_tensor_layout* t[3] = {&L.gate, &L.up, &L.down};
+  MatPlan* m[3] = {&P->gate, &P->up, &P->down};
+  for (int i = 0; i < 3; ++i)
+    if (!plan_matrix((int)t[i]->rows, (int)t[i]->cols, (int)bits, t[i]->codes_offset,
+                     t[i]->scales_offset, m[i]))
+      return fail(SMOE_E_UNSUPPORTED,
+                  "no kernel for a [%u, %u] Q%u tensor (row of %u code words)", t[i]->rows,
+                  t[i]->cols, bits, t[i]->cols * bits / 32);
+  if (Lout) *Lout = L;
+  return SMOE_OK;
+}
+
+WsLayout ws_layout(const LayerInfo& L, int T, int k) {
+  WsLayout W{};
+  const uint64_t P = (uint64_t)T * k, E = L.desc.num_experts;
+  uint64_t o = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  W.ids = take(P * 4);
+  W.w = take(P * 4);
+  W.meta = take(64);
+  W.active = take(E * 4);
+  W.offs = take((E + 1) * 4);
+  W.pair_token = take(P * 4);
+  W.pair_of = take(P * 4);
+  W.h = take(P * L.desc.ffn_dim * 4);
+  W.y = take(P * L.desc.d_model * 4);
+  W.h_shared = take((uint64_t)T * L.desc.shared_ffn_dim * 4);
+  W.y_shared = take(L.desc.shared_ffn_dim ? (uint64_t)T * L.desc.d_model * 4 : 0);
+  W.total = o;
+  return W;
+}
+
+int check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SMOE_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return SMOE_OK;
+}
+
+// One layer: route+group, gate/up+SwiGLU, down, combine (optionally into the
+// residual stream with RMSNorm applied on the way in).
+int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const float* logits,
+                 int T, int k, int norm, float* out, int accumulate, int32_t* uids, float* uw,
+                 uint8_t* ws, hipStream_t s) {
+  const WsLayout W = ws_layout(L, T, k);
+  int32_t* ids = (int32_t*)(ws + W.ids);
+  float* w = (float*)(ws + W.w);
+  int* meta = (int*)(ws + W.meta);
+  int* active = (int*)(ws + W.active);
+  int* offs = (int*)(ws + W.offs);
+  int* pair_token = (int*)(ws + W.pair_token);
+  int* pair_of = (int*)(ws + W.pair_of);
+  float* h = (float*)(ws + W.h);
+  float* y = (float*)(ws + W.y);
+  const int E = (int)L.desc.num_experts;
+  const int max_slots = T * k < E ? T * k : E;
+  int rc;
+  if ((rc = check_hip(launch_route(logits, T, E, k, norm, ids, w, uids, uw, 1, meta, active,
+                                   offs, pair_token, pair_of, s),
+                      "route launch")))
+    return rc;
+  if ((rc = check_hip(launch_gate_up(L, false, x, xmode, eps, T, max_slots, meta, active, offs,
+                                     pair_token, h, s),
+                      "gate/up launch")))
+    return rc;
+  float* ysh = nullptr;
+  if (L.desc.shared_ffn_dim) {
+    float* hsh = (float*)(ws + W.h_shared);
+    ysh = (float*)(ws + W.y_shared);
+    if ((rc = check_hip(launch_gate_up(L, true, x, xmode, eps, T, 1, meta, active, offs,
+                                       pair_token, hsh, s),
+                        "shared gate/up launch")))
+      return rc;
+    if ((rc = check_hip(launch_down(L, true, hsh, T, 1, meta, active, offs, ysh, s),
+                        "shared down launch")))
+      return rc;
+  }
+  if ((rc = check_hip(launch_down(L, false, h, T, max_slots, meta, active, offs, y, s),
+                      "down launch")))
+    return rc;
+  return check_hip(
+      launch_combine(y, pair_of, w, ysh, out, T, k, (int)L.desc.d_model, accumulate, s),
+      "combine launch");
+}
+
+}  // namespace
+}  // namespace smoe
+
+using namespace smoe;
+
+extern "C" {
+
+int smoe_version(void) { return SMOE_ABI_VERSION; }
+
+const char* smoe_last_error(void) { return g_err; }
+
+int smoe_expert_layout_of(uint32_t d_model, uint32_t ffn_dim, uint32_t bits,
+                          uint32_t scale_dtype, smoe_expert_layout* out) {
+  int rc = layout_of(d_model, ffn_dim, bits, scale_dtype, out);
+  return rc ? rc : ok();
+}
+
+int smoe_load_blobs(const smoe_layer_desc* desc, const void* d_blobs, uint64_t nbytes,
+                    const void* d_shared_blob, uint64_t shared_nbytes, smoe_layer** out) {
+  if (!out) return fail(SMOE_E_ARG, "null output handle pointer");
+  *out = nullptr;
+  if (!desc) return fail(SMOE_E_ARG, "null layer description");
+  if (!d_blobs) return fail(SMOE_E_ARG, "null blob bank");
+  const smoe_layer_desc& D = *desc;
+  if (D.group_size != SMOE_GROUP_SIZE)
+    return fail(SMOE_E_ARG, "group_size must be 64 (got %u)", D.group_size);
+  if (D.num_experts < 1 || D.num_experts > SMOE_MAX_EXPERTS)
+    return fail(SMOE_E_ARG, "num_experts must be in [1, %d] (got %u)", SMOE_MAX_EXPERTS,
+                D.num_experts);
+  if (D.reserved != 0) return fail(SMOE_E_ARG, "reserved field must be 0");
+  LayerInfo info{};
+  info.desc = D;
+  smoe_expert_layout L;
+  int rc = make_plan(D.d_model, D.ffn_dim, D.bits, D.scale_dtype, &info.plan, &L);
+  if (rc) return rc;
+  if (D.blob_stride % SMOE_BLOB_ALIGN || D.blob_stride < L.raw_size)
+    return fail(SMOE_E_LAYOUT,
+                "blob_stride %llu must be a multiple of 16384 and >= the raw blob size %llu",
+                (unsigned long long)D.blob_stride, (unsigned long long)L.raw_size);
+  if (!aligned(d_blobs, SMOE_BANK_ALIGN))
+    return fail(SMOE_E_LAYOUT, "blob bank must be %d-byte aligned", SMOE_BANK_ALIGN);
+  const uint64_t need = (uint64_t)(D.num_experts - 1) * D.blob_stride + L.raw_size;
+  if (nbytes < need)
+    return fail(SMOE_E_LAYOUT, "blob bank holds %llu bytes, needs %llu",
+                (unsigned long long)nbytes, (unsigned long long)need);
+  info.blobs = (const uint8_t*)d_blobs;
+  info.nbytes = nbytes;
+  if (D.shared_ffn_dim) {
+    if (!d_shared_blob) return fail(SMOE_E_ARG, "shared_ffn_dim set but no shared blob");
+    smoe_expert_layout SL;
+    rc = make_plan(D.d_model, D.shared_ffn_dim, D.bits, D.scale_dtype, &info.shared_plan, &SL);
+    if (rc) return rc;
+    if (!aligned(d_shared_blob, SMOE_BANK_ALIGN))
+      return fail(SMOE_E_LAYOUT, "shared blob must be %d-byte aligned", SMOE_BANK_ALIGN);
+    if (shared_nbytes < SL.raw_size)
+      return fail(SMOE_E_LAYOUT, "shared blob holds %llu bytes, needs %llu",
+                  (unsigned long long)shared_nbytes, (unsigned long long)SL.raw_size);
+    info.shared = (const uint8_t*)d_shared_blob;
+    info.shared_nbytes = shared_nbytes;
+  } else if (d_shared_blob) {
+    return fail(SMOE_E_ARG, "shared blob given but shared_ffn_dim is 0");
+  }
+  smoe_layer* h = new (std::nothrow) smoe_layer;
+  if (!h) return fail(SMOE_E_ARG, "out of host memory");
+  h->info = info;
+  *out = h;
+  return ok();
+}
+
+void smoe_free(smoe_layer* layer) { delete layer; }
+
+uint64_t smoe_workspace_bytes(const smoe_layer* layer, int n_tokens, int top_k) {
+  if (!layer || n_tokens < 0 || n_tokens > SMOE_MAX_TOKENS || top_k < 1 ||
+      top_k > SMOE_MAX_TOP_K)
+    return 0;
+  return ws_layout(layer->info, n_tokens, top_k).total;
+}
+
+int smoe_route(const float* d_logits, int n_tokens, int n_experts, int top_k,
+               int norm_topk_prob, int32_t* d_ids, float* d_weights, void* hip_stream) {
+  if (n_tokens < 0 || n_tokens > SMOE_MAX_TOKENS)
+    return fail(SMOE_E_ARG, "n_tokens must be in [0, %d]", SMOE_MAX_TOKENS);
+  if (n_experts < 1 || n_experts > SMOE_MAX_EXPERTS)
+    return fail(SMOE_E_ARG, "n_experts must be in [1, %d]", SMOE_MAX_EXPERTS);
+  const int kmax = n_experts < SMOE_MAX_TOP_K ? n_experts : SMOE_MAX_TOP_K;
+  if (top_k < 1 || top_k > kmax) return fail(SMOE_E_ARG, "top_k must be in [1, %d]", kmax);
+  if (n_tokens == 0) return ok();
+  if (!d_logits || !d_ids || !d_weights) return fail(SMOE_E_ARG, "null pointer argument");
+  int rc = check_hip(launch_route(d_logits, n_tokens, n_experts, top_k, norm_topk_prob != 0,
+                                  d_ids, d_weights, nullptr, nullptr, 0, nullptr, nullptr,
+                                  nullptr, nullptr, nullptr, (hipStream_t)hip_stream),
+                     "route launch");
+  return rc ? rc : ok();
+}
+
+static int check_forward_args(const smoe_layer* layer, int n_tokens, int top_k,
+                              const void* d_workspace, uint64_t ws_bytes) {
+  if (!layer) return fail(SMOE_E_ARG, "null layer");
+  if (n_tokens < 0 || n_tokens > SMOE_MAX_TOKENS)
+    return fail(SMOE_E_ARG, "n_tokens must be in [0, %d] (got %d)", SMOE_MAX_TOKENS, n_tokens);
+  const int E = (int)layer->info.desc.num_experts;
+  const int kmax = E < SMOE_MAX_TOP_K ? E : SMOE_MAX_TOP_K;
+  if (top_k < 1 || top_k > kmax)
+    return fail(SMOE_E_ARG, "top_k must be in [1, %d] (got %d)", kmax, top_k);
+  if (n_tokens == 0) return SMOE_OK;
+  // the grouping step keeps an expert x token bitmask in LDS (<= 64 KB)
+  const uint64_t lds = (uint64_t)E * ((n_tokens + 31) / 32) * 4 + (uint64_t)E * 8;
+  if (lds > 65536)
+    return fail(SMOE_E_UNSUPPORTED, "%d experts x %d tokens exceed the grouping limit", E,
+                n_tokens);
+  const uint64_t need = ws_layout(layer->info, n_tokens, top_k).total;
+  if (!d_workspace || ws_bytes < need)
+    return fail(SMOE_E_WORKSPACE, "workspace of %llu bytes needed (got %llu)",
+                (unsigned long long)need, (unsigned long long)ws_bytes);
+  if (!aligned(d_workspace, 256)) return fail(SMOE_E_WORKSPACE, "workspace must be 256-byte aligned");
+  return SMOE_OK;
+}
+
+int smoe_moe_forward(const smoe_layer* layer, const void* d_x, int x_dtype,
+                     const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
+                     float* d_out, int32_t* d_topk_ids, float* d_topk_w, void* d_workspace,
+                     uint64_t ws_bytes, void* hip_stream) {
+  int rc = check_forward_args(layer, n_tokens, top_k, d_workspace, ws_bytes);
+  if (rc) return rc;
+  if (x_dtype != SMOE_DTYPE_BF16 && x_dtype != SMOE_DTYPE_F32)
+    return fail(SMOE_E_ARG, "x_dtype must be SMOE_DTYPE_BF16 or SMOE_DTYPE_F32");
+  if (n_tokens == 0) return ok();
+  if (!d_x || !d_logits || !d_out) return fail(SMOE_E_ARG, "null x, logits or out");
+  if (!aligned(d_x, 16)) return fail(SMOE_E_ARG, "x must be 16-byte aligned");
+  if (!aligned(d_logits, 4) || !aligned(d_out, 4))
+    return fail(SMOE_E_ARG, "logits and out must be 4-byte aligned");
+  rc = forward_impl(layer->info, d_x, x_dtype == SMOE_DTYPE_BF16 ? X_BF16 : X_F32, 0.f,
+                    d_logits, n_tokens, top_k, norm_topk_prob != 0, d_out, 0, d_topk_ids,
+                    d_topk_w, (uint8_t*)d_workspace, (hipStream_t)hip_stream);
+  return rc ? rc : ok();
+}
+
+int smoe_decode_step(const smoe_layer* const* layers, int n_layers, float* d_h,
+                     const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
+                     float eps, void* d_workspace, uint64_t ws_bytes, void* hip_stream) {
+  if (!layers || n_layers < 1) return fail(SMOE_E_ARG, "need at least one layer");
+  if (!(eps > 0.f)) return fail(SMOE_E_ARG, "eps must be positive");
+  const uint32_t d = layers[0] ? layers[0]->info.desc.d_model : 0;
+  for (int l = 0; l < n_layers; ++l) {
+    int rc = check_forward_args(layers[l], n_tokens, top_k, d_workspace, ws_bytes);
+    if (rc) return rc;
+    if (layers[l]->info.desc.d_model != d)
+      return fail(SMOE_E_ARG, "layer %d has d_model %u, expected %u", l,
+                  layers[l]->info.desc.d_model, d);
+  }
+  if (n_tokens == 0) return ok();
+  if (!d_h || !d_logits) return fail(SMOE_E_ARG, "null h or logits");
+  if (!aligned(d_h, 16) || !aligned(d_logits, 4))
+    return fail(SMOE_E_ARG, "h must be 16-byte and logits 4-byte aligned");
+  for (int l = 0; l < n_layers; ++l) {
+    const LayerInfo& L = layers[l]->info;
+    const float* lg = d_logits + (size_t)l * n_tokens * L.desc.num_experts;
+    int rc = forward_impl(L, d_h, X_F32_RMS, eps, lg, n_tokens, top_k, norm_topk_prob != 0, d_h,
+                          1, nullptr, nullptr, (uint8_t*)d_workspace, (hipStream_t)hip_stream);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal interface between the host API (smoe_api.hip) and the kernel
+// launchers (smoe_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/smoe.h"
+
+namespace smoe {
+
+// How one weight matrix is walked by a wavefront: each row of W = cols*bits/32
+// 32-bit code words is split over LPR = 2^lpr_log2 lanes holding V words each
+// (W == LPR * V); a wave therefore covers 64 / LPR rows per load.
+struct MatPlan {
+  uint64_t codes_off;   // byte offset of the codes inside the blob
+  uint64_t scales_off;  // byte offset of the scales inside the blob
+  int rows, cols;
+  int words_per_row;    // W
+  int v;                // words per lane
+  int lpr_log2;
+};
+
+struct ExpertPlan {
+  int d_model, ffn;
+  MatPlan gate, up, down;
+  uint64_t raw_size, padded_size;
+};
+
+// Result of planning one matrix; returns false if no kernel exists for it.
+bool plan_matrix(int rows, int cols, int bits, uint64_t codes_off, uint64_t scales_off,
+                 MatPlan* out);
+
+// Workspace layout of one forward (offsets in bytes from the workspace base).
+struct WsLayout {
+  uint64_t ids, w, meta, active, offs, pair_token, pair_of;
+  uint64_t h, y, h_shared, y_shared;
+  uint64_t total;
+};
+
+struct LayerInfo {
+  smoe_layer_desc desc;
+  const uint8_t* blobs;
+  uint64_t nbytes;
+  const uint8_t* shared;
+  uint64_t shared_nbytes;
+  ExpertPlan plan;
+  ExpertPlan shared_plan;  // valid when desc.shared_ffn_dim > 0
+};
+
+// Input description for the gate/up stage.
+enum XMode : int {
+  X_BF16 = 0,       // bf16 activations
+  X_F32 = 1,        // fp32 activations
+  X_F32_RMS = 2,    // fp32 residual stream; the stage applies unit-gain RMSNorm
+};
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int32_t* ids,
+                        float* w, int32_t* user_ids, float* user_w, int group, int* meta,
+                        int* active, int* offs, int* pair_token, int* pair_of,
+                        hipStream_t stream);
+
+hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xmode,
+                          float rms_eps, int T, int max_slots, const int* meta,
+                          const int* active, const int* offs, const int* pair_token,
+                          float* h, hipStream_t stream);
+
+hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int max_slots,
+                       const int* meta, const int* active, const int* offs, float* y,
+                       hipStream_t stream);
+
+hipError_t launch_combine(const float* y, const int* pair_of, const float* w,
+                          const float* y_shared, float* out, int T, int k, int d,
+                          int accumulate, hipStream_t stream);
+
+}  // namespace smoe

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Bars: routing ids bit-exact (set and order, ties to the lower id); routing
+weights within 1e-5 relative (fp32 exp against the oracle's fp64); layer
+outputs within 1e-3 relative L2, overall and per token.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from helpers import DeviceLayer, random_layer, rel_l2, tiny_swiglu_layer
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def _x(r, T, d, dtype):
+    x = synth.normal_f32(r, (T, d))
+    return synth.round_to_bf16(x) if dtype == "bf16" else x
+
+
+def _check_layer(hl, x, logits, k, norm, x_dtype, tokens=None, dl=None):
+    dl = dl or DeviceLayer(hl)
+    out, ids, w = dl.forward(x, logits, k, norm, x_dtype)
+    ref, rids, rw = O.moe_forward(hl.oracle(), x, logits, k, norm, tokens=tokens)
+    toks = list(range(x.shape[0])) if tokens is None else list(tokens)
+    # routing of every token is exact
+    for t in range(x.shape[0]):
+        want, wt = O.route(logits[t], k, norm)
+        assert ids[t].tolist() == want, (t, ids[t], want)
+        assert np.allclose(w[t], wt, rtol=1e-5, atol=1e-7), (t, w[t], wt)
+    sel = out[toks]
+    assert np.all(np.isfinite(sel))
+    err = rel_l2(sel, ref)
+    per_tok = [rel_l2(sel[i], ref[i]) for i in range(len(toks))]
+    assert err <= TOL and max(per_tok) <= TOL, (err, max(per_tok))
+    return err
+
+
+# ------------------------------------------------------------------ routing --
+
+@pytest.mark.parametrize("T,E,k,norm", [(1, 128, 8, True), (32, 128, 8, True), (8, 64, 6, False),
+                                        (5, 8, 8, True), (3, 1, 1, True), (17, 512, 16, False),
+                                        (1024, 128, 8, True)])
+def test_route_matches_oracle(T, E, k, norm):
+    torch = _torch()
+    import quantised_moe_expert_amd as smoe
+    r = synth.rng(100 + T + E)
+    lg = synth.normal_f32(r, (T, E))
+    d_lg = torch.from_numpy(lg).cuda()
+    ids = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    smoe.smoe_route(d_lg.data_ptr(), T, E, k, norm, ids.data_ptr(), w.data_ptr(),
+                    torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ids, w = ids.cpu().numpy(), w.cpu().numpy()
+    for t in range(T):
+        want, wt = O.route(lg[t], k, norm)
+        assert ids[t].tolist() == want
+        assert np.allclose(w[t], wt, rtol=1e-5, atol=1e-7)
+
+
+def test_route_ties_go_to_lower_id():
+    torch = _torch()
+    import quantised_moe_expert_amd as smoe
+    r = synth.rng(7)
+    T, E, k = 64, 128, 8
+    lg = (r.integers(0, 3, (T, E)) * 0.5).astype(np.float32)  # massive ties
+    lg[3] = 0.0                                               # all equal
+    d_lg = torch.from_numpy(lg).cuda()
+    ids = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    smoe.smoe_route(d_lg.data_ptr(), T, E, k, True, ids.data_ptr(), w.data_ptr(), 0)
+    torch.cuda.synchronize()
+    ids = ids.cpu().numpy()
+    for t in range(T):
+        assert ids[t].tolist() == O.route(lg[t], k, True)[0]
+    assert ids[3].tolist() == list(range(8))
+
+
+# ------------------------------------------------------- small full parity --
+
+SMALL = [
+    # d, ffn, E, k, T, bits, scales, norm, shared
+    (512, 320, 16, 4, 5, 4, "f32", True, 0),
+    (512, 320, 16, 4, 5, 2, "f16", False, 0),
+    (192, 64, 8, 8, 3, 4, "f16", True, 128),
+    (1024, 192, 32, 16, 9, 2, "f32", True, 0),
+    (256, 128, 1, 1, 1, 4, "f32", True, 0),
+    (2048, 1408, 4, 2, 2, 4, "f32", False, 2816),
+    (2048, 1408, 6, 3, 3, 2, "f16", True, 2816),
+    (640, 448, 12, 5, 7, 4, "f32", True, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"d{c[0]}_f{c[1]}_E{c[2]}_k{c[3]}_T{c[4]}_q{c[5]}"
+                                            f"_{c[6]}_n{int(c[7])}_s{c[8]}" for c in SMALL])
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_small_layers(case, x_dtype):
+    _torch()
+    d, ffn, E, k, T, bits, sd, norm, shared = case
+    hl = random_layer(1000 + d + ffn + E, d, ffn, E, bits, sd, shared)
+    r = synth.rng(55 + T)
+    x = _x(r, T, d, x_dtype)
+    lg = synth.normal_f32(r, (T, E))
+    _check_layer(hl, x, lg, k, norm, x_dtype)
+
+
+def test_stride_larger_than_padded_blob():
+    _torch()
+    hl = random_layer(5, 512, 320, 8, 4, "f32", stride_extra_pages=3)
+    r = synth.rng(6)
+    x = _x(r, 4, 512, "bf16")
+    _check_layer(hl, x, synth.normal_f32(r, (4, 8)), 3, True, "bf16")
+
+
+def test_zero_tokens_is_a_no_op():
+    torch = _torch()
+    import quantised_moe_expert_amd as smoe
+    hl = random_layer(9, 256, 128, 4, 4)
+    dl = DeviceLayer(hl)
+    out = torch.full((1, 256), 3.0, device="cuda")
+    smoe.smoe_moe_forward(dl.handle, 0, smoe.SMOE_DTYPE_BF16, 0, 0, 2, True, out.data_ptr(), 0, 0,
+                          0, 0, 0)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+
+
+def test_repeat_calls_are_bitwise_identical():
+    _torch()
+    hl = random_layer(11, 1024, 320, 16, 4)
+    r = synth.rng(12)
+    x = _x(r, 6, 1024, "bf16")
+    lg = synth.normal_f32(r, (6, 16))
+    dl = DeviceLayer(hl)
+    a = dl.forward(x, lg, 4, True)[0]
+    b = dl.forward(x, lg, 4, True)[0]
+    assert np.array_equal(a, b)
+
+
+def test_activation_range_is_scale_free():
+    # outputs scale linearly with x; the per-vector power-of-two rescale keeps
+    # fp16 in range for large and tiny activations
+    _torch()
+    hl = random_layer(13, 512, 320, 8, 4)
+    dl = DeviceLayer(hl)
+    r = synth.rng(14)
+    x = synth.normal_f32(r, (2, 512))
+    lg = synth.normal_f32(r, (2, 8))
+    for s in (2.0 ** 40, 2.0 ** -40):
+        xs = (x * np.float32(s)).astype(np.float32)
+        out = dl.forward(xs, lg, 2, True, "f32")[0]
+        ref = O.moe_forward(hl.oracle(), xs, lg, 2, True)[0]
+        assert rel_l2(out, ref) <= TOL
+
+
+# ------------------------------------------------------------ the workloads --
+
+def test_tiny_swiglu_workload():
+    _torch()
+    x, hl = tiny_swiglu_layer(0)
+    _check_layer(hl, x, np.zeros((1, 1), np.float32), 1, True, "f32")
+
+
+def test_qwen235b_q4_b1_full():
+    _torch()
+    W = synth.WORKLOADS["qwen235b_q4_b1"]
+    hl = random_layer(W.seed, W.d_model, W.ffn_dim, W.num_experts, W.bits)
+    r = synth.rng(W.seed + 1000)
+    x = _x(r, 1, W.d_model, "bf16")
+    lg = synth.normal_f32(r, (1, W.num_experts))
+    _check_layer(hl, x, lg, W.top_k, W.norm_topk_prob, "bf16")
+
+
+@pytest.mark.parametrize("name", ["qwen235b_q4_b32", "qwen235b_q2_b32"])
+def test_qwen235b_b32_sampled(name):
+    _torch()
+    W = synth.WORKLOADS[name]
+    hl = random_layer(W.seed + W.bits, W.d_model, W.ffn_dim, W.num_experts, W.bits)
+    r = synth.rng(W.seed + 2000)
+    x = _x(r, W.n_tokens, W.d_model, "bf16")
+    lg = synth.normal_f32(r, (W.n_tokens, W.num_experts))
+    _check_layer(hl, x, lg, W.top_k, W.norm_topk_prob, "bf16", tokens=[0, 13, 31])
+
+
+def test_deepseek16b_q4_b8_full():
+    _torch()
+    W = synth.WORKLOADS["deepseek16b_q4_b8"]
+    hl = random_layer(W.seed, W.d_model, W.ffn_dim, W.num_experts, W.bits,
+                      shared_ffn=W.shared_ffn_dim)
+    r = synth.rng(W.seed + 3000)
+    x = _x(r, W.n_tokens, W.d_model, "bf16")
+    lg = synth.normal_f32(r, (W.n_tokens, W.num_experts))
+    _check_layer(hl, x, lg, W.top_k, W.norm_topk_prob, "bf16")
+
+
+def test_qwen_stack_three_layers_full_width():
+    torch = _torch()
+    import quantised_moe_expert_amd as smoe
+    W = synth.WORKLOADS["qwen235b_q4_stack94"]
+    nl = 3
+    hls = [random_layer(W.seed * 100 + l, W.d_model, W.ffn_dim, W.num_experts, W.bits)
+           for l in range(nl)]
+    r = synth.rng(W.seed + 4000)
+    x = synth.normal_f32(r, (1, W.d_model))
+    lg = synth.normal_f32(r, (nl, 1, W.num_experts))
+    dls = [DeviceLayer(h) for h in hls]
+    h_d = torch.from_numpy(x.copy()).cuda()
+    lg_d = torch.from_numpy(lg).cuda()
+    nws = smoe.smoe_workspace_bytes(dls[0].handle, 1, W.top_k)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    smoe.smoe_decode_step([d.handle for d in dls], h_d.data_ptr(), lg_d.data_ptr(), 1, W.top_k,
+                          True, 1e-6, ws.data_ptr(), nws, 0)
+    torch.cuda.synchronize()
+    got = h_d.cpu().numpy()
+    ref = O.decode_step([h.oracle() for h in hls], x, list(lg), W.top_k, True, 1e-6)
+    assert rel_l2(got, ref) <= TOL
+    assert rel_l2(got - x, ref - x) <= TOL   # the accumulated MoE delta
