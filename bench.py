@@ -158,6 +158,10 @@ def main():
     pairs = T * k * W.n_layers
     avg_unique = sum(uniq[(args.warmup + i) % n_logit_sets] for i in range(args.steps)) / args.steps
 
+    single = T == 1 and not W.shared_ffn_dim and os.environ.get("SMOE_FORCE_MULTI_KERNEL") != "1"
+    kernel_label = ("k_decode1: one launch per layer (events around the timed loop of "
+                    "back-to-back launches)" if single else
+                    "whole forward (route, gate/up, down, combine launches)")
     result = {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
@@ -185,7 +189,7 @@ def main():
         "wall_s_timed": round(t_wall, 3),
         "roofline": {
             "bound": "hbm",
-            "kernel": "whole forward (route, gate/up, down, combine launches)",
+            "kernel": kernel_label,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

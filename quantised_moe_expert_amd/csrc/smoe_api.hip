@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <new>
@@ -21,6 +22,13 @@ namespace smoe {
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Set from the environment at load: SMOE_FORCE_MULTI_KERNEL=1 makes batch-1
+// calls take the multi-kernel path (used to test both paths).
+const bool g_force_multi = [] {
+  const char* v = getenv("SMOE_FORCE_MULTI_KERNEL");
+  return v && v[0] == '1';
+}();
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -136,6 +144,14 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
   const int E = (int)L.desc.num_experts;
   const int max_slots = T * k < E ? T * k : E;
   int rc;
+  if (T == 1 && !g_force_multi) {
+    bool launched = false;
+    if ((rc = check_hip(decode1_try(L, x, xmode != X_BF16, xmode == X_F32_RMS, eps, logits, k,
+                                    norm, out, accumulate, uids, uw, h, ids, w, s, &launched),
+                        "batch-1 layer")))
+      return rc;
+    if (launched) return SMOE_OK;
+  }
   if ((rc = check_hip(launch_route(logits, T, E, k, norm, ids, w, uids, uw, 1, meta, active,
                                    offs, pair_token, pair_of, s),
                       "route launch")))

@@ -1,0 +1,116 @@
+// Host side of the batch-1 layer kernels: picks the instantiations for a
+// layer's shape and enqueues the two launches. Returns "not launched" (so the
+// caller takes the multi-kernel grouped path) when no instantiation fits.
+
+#include <hip/hip_runtime.h>
+
+#include "smoe_decode_args.hpp"
+#include "smoe_internal.hpp"
+
+namespace smoe {
+namespace {
+
+typedef hipError_t (*GuLaunch)(const DecodeArgs&, int, hipStream_t);
+typedef hipError_t (*DnLaunch)(const DecodeArgs&, int, hipStream_t);
+
+template <int BITS, typename ST>
+bool find_gu(int vg, bool xf32, GuLaunch* L) {
+#define SMOE_FIND_G(v)                                                        \
+  if (vg == v) {                                                             \
+    *L = xf32 ? launch_dec_gate_up<BITS, ST, v, true>                        \
+              : launch_dec_gate_up<BITS, ST, v, false>;                      \
+    return true;                                                             \
+  }
+  if constexpr (BITS == 4) {
+    SMOE_DEC_Q4_VG(SMOE_FIND_G)
+  } else {
+    SMOE_DEC_Q2_VG(SMOE_FIND_G)
+  }
+#undef SMOE_FIND_G
+  return false;
+}
+
+template <int BITS, typename ST>
+bool find_dn(int vd, DnLaunch* L) {
+#define SMOE_FIND_D(v)                 \
+  if (vd == v) {                       \
+    *L = launch_dec_down<BITS, ST, v>; \
+    return true;                       \
+  }
+  if constexpr (BITS == 4) {
+    SMOE_DEC_Q4_VD(SMOE_FIND_D)
+  } else {
+    SMOE_DEC_Q2_VD(SMOE_FIND_D)
+  }
+#undef SMOE_FIND_D
+  return false;
+}
+
+bool find_pair(int bits, int sdt, int vg, int vd, bool xf32, GuLaunch* G, DnLaunch* D) {
+  if (bits == 4 && sdt == SMOE_SCALE_F32)
+    return find_gu<4, float>(vg, xf32, G) && find_dn<4, float>(vd, D);
+  if (bits == 4) return find_gu<4, _Float16>(vg, xf32, G) && find_dn<4, _Float16>(vd, D);
+  if (sdt == SMOE_SCALE_F32) return find_gu<2, float>(vg, xf32, G) && find_dn<2, float>(vd, D);
+  return find_gu<2, _Float16>(vg, xf32, G) && find_dn<2, _Float16>(vd, D);
+}
+
+}  // namespace
+
+hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, float eps,
+                       const float* logits, int k, int norm, float* out, int accumulate,
+                       int32_t* uids, float* uw, float* h, int32_t* ws_ids, float* ws_w,
+                       hipStream_t stream, bool* launched) {
+  *launched = false;
+  if (L.desc.shared_ffn_dim) return hipSuccess;
+  const ExpertPlan& P = L.plan;
+  const int bits = (int)L.desc.bits;
+  GuLaunch gu;
+  DnLaunch dn;
+  if (!find_pair(bits, (int)L.desc.scale_dtype, P.gate.v, P.down.v, xf32, &gu, &dn))
+    return hipSuccess;
+  const int rpwd = 64 >> P.down.lpr_log2;
+  int rb = (P.d_model + DEC_NWG - 1) / DEC_NWG;
+  rb = (rb + rpwd - 1) / rpwd * rpwd;
+  // shape limits of the kernels' register and LDS staging
+  if (rb > DEC_RB_MAX) return hipSuccess;
+  if ((int64_t)P.d_model * bits / 32 > (int64_t)DEC_XW * DEC_THREADS) return hipSuccess;
+  if ((int64_t)P.ffn * bits / 32 > 64 * (DEC_HC / (bits == 2 ? 2 : 1))) return hipSuccess;
+  if ((int64_t)k * P.ffn / 2 > DEC_H_LDS) return hipSuccess;
+  if (k > DEC_HJ * (DEC_THREADS / 64)) return hipSuccess;
+  DecodeArgs A{};
+  A.blobs = L.blobs;
+  A.stride = L.desc.blob_stride;
+  A.gc = P.gate.codes_off;
+  A.gs = P.gate.scales_off;
+  A.uc = P.up.codes_off;
+  A.us = P.up.scales_off;
+  A.dc = P.down.codes_off;
+  A.ds = P.down.scales_off;
+  A.d = P.d_model;
+  A.ffn = P.ffn;
+  A.E = (int)L.desc.num_experts;
+  A.k = k;
+  A.norm = norm;
+  A.lg_g = P.gate.lpr_log2;
+  A.lg_d = P.down.lpr_log2;
+  A.x = x;
+  A.rms = rms ? 1 : 0;
+  A.eps = eps;
+  A.logits = logits;
+  A.h = h;
+  A.ws_ids = ws_ids;
+  A.ws_w = ws_w;
+  A.out = out;
+  A.accumulate = accumulate;
+  A.user_ids = uids;
+  A.user_w = uw;
+  A.rb = rb;
+  hipError_t e = gu(A, DEC_NWG, stream);
+  if (e != hipSuccess) return e;
+  e = dn(A, DEC_NWG, stream);
+  if (e != hipSuccess) return e;
+  *launched = true;
+  return hipSuccess;
+}
+
+}  // namespace smoe

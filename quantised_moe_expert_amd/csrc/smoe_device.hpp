@@ -94,34 +94,55 @@ __device__ __forceinline__ float lane63(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Lane <-> code-word map of one row of W = LPR * V 32-bit code words spread
+// over LPR lanes. A lane's V words come as N4 = V / 4 chunks of four words and
+// a tail of R = V % 4 words: chunk c of lane lr holds words
+// c*4*LPR + 4*lr + [0, 4), the tail holds words 4*N4*LPR + R*lr + [0, R).
+// Each load instruction therefore reads one contiguous span across the lanes
+// of a row (16-byte chunks, then 4/8/12-byte tails). Slot s of a lane is its
+// s-th word in this order.
 template <int V>
-__device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint32_t (&w)[V]) {
-#pragma unroll
-  for (int i = 0; i < V / 4; ++i) {
-    u32x4 t = *(const u32x4_a4*)(p + 4 * i);
-    w[4 * i + 0] = t.x;
-    w[4 * i + 1] = t.y;
-    w[4 * i + 2] = t.z;
-    w[4 * i + 3] = t.w;
+struct LaneMap {
+  static constexpr int N4 = V / 4;
+  static constexpr int R = V % 4;
+  static __device__ __forceinline__ int word(int lr, int LPR, int s) {
+    return s < 4 * N4 ? (s >> 2) * 4 * LPR + 4 * lr + (s & 3)
+                      : 4 * N4 * LPR + R * lr + (s - 4 * N4);
   }
-  constexpr int B = V - V % 4;
-  if constexpr (V % 4 == 3) {
-    u32x3 t = *(const u32x3_a4*)(p + B);
+};
+
+template <int V, bool NT>
+__device__ __forceinline__ void load_row_words(const uint32_t* __restrict__ row, int lr, int LPR,
+                                               uint32_t (&w)[V]) {
+  using LM = LaneMap<V>;
+#pragma unroll
+  for (int c = 0; c < LM::N4; ++c) {
+    const u32x4_a4* p = (const u32x4_a4*)(row + c * 4 * LPR + 4 * lr);
+    const u32x4 t = NT ? __builtin_nontemporal_load(p) : *p;
+    w[4 * c + 0] = t.x;
+    w[4 * c + 1] = t.y;
+    w[4 * c + 2] = t.z;
+    w[4 * c + 3] = t.w;
+  }
+  constexpr int B = 4 * LM::N4;
+  const uint32_t* tail = row + B * LPR + LM::R * lr;
+  if constexpr (LM::R == 3) {
+    const u32x3 t = NT ? __builtin_nontemporal_load((const u32x3_a4*)tail) : *(const u32x3_a4*)tail;
     w[B] = t.x;
     w[B + 1] = t.y;
     w[B + 2] = t.z;
-  } else if constexpr (V % 4 == 2) {
-    u32x2 t = *(const u32x2_a4*)(p + B);
+  } else if constexpr (LM::R == 2) {
+    const u32x2 t = NT ? __builtin_nontemporal_load((const u32x2_a4*)tail) : *(const u32x2_a4*)tail;
     w[B] = t.x;
     w[B + 1] = t.y;
-  } else if constexpr (V % 4 == 1) {
-    w[B] = p[B];
+  } else if constexpr (LM::R == 1) {
+    w[B] = NT ? __builtin_nontemporal_load(tail) : *tail;
   }
 }
 
-template <typename ST>
+template <typename ST, bool NT>
 __device__ __forceinline__ float load_scale(const ST* p) {
-  return (float)*p;
+  return NT ? (float)__builtin_nontemporal_load(p) : (float)*p;
 }
 
 // Sum over one code word of (code_i - m) * x_i (up to the K offset, which the
@@ -152,8 +173,8 @@ struct XRegs {
   float oscale;  // multiply a reduced row sum by this
 };
 
-// Reads the lane's V*WPW activations (columns [lr*V*WPW, ...)) from a bf16 or
-// fp32 vector, rescales by a power of two, optionally applies unit-gain
+// Reads the lane's V*WPW activations (the columns of its code words, see
+// LaneMap) from a bf16 or fp32 vector, rescales by a power of two, optionally applies unit-gain
 // RMSNorm (as a factor on the output), and builds the fp16 pairs and K.
 template <int BITS, int V, bool SPLIT, bool BF16>
 __device__ __forceinline__ void prep_x(XRegs<BITS, V, SPLIT>& X, const void* vec, int lr,
@@ -161,10 +182,11 @@ __device__ __forceinline__ void prep_x(XRegs<BITS, V, SPLIT>& X, const void* vec
   constexpr int WPW = QT<BITS>::WPW;
   constexpr int NPOS = QT<BITS>::NPOS;
   constexpr int PPW = QT<BITS>::PPW;
-  const int col0 = lr * V * WPW;
+  const int LPR = 1 << lg;
   auto load_word_vals = [&](int w, float (&xv)[WPW]) {
+    const int col0 = LaneMap<V>::word(lr, LPR, w) * WPW;
     if constexpr (BF16) {
-      const uint32_t* p = (const uint32_t*)((const uint16_t*)vec + col0 + w * WPW);
+      const uint32_t* p = (const uint32_t*)((const uint16_t*)vec + col0);
 #pragma unroll
       for (int i = 0; i < WPW / 8; ++i) {
         u32x4 t = *(const u32x4_a4*)(p + 4 * i);
@@ -176,7 +198,7 @@ __device__ __forceinline__ void prep_x(XRegs<BITS, V, SPLIT>& X, const void* vec
         }
       }
     } else {
-      const float* p = (const float*)vec + col0 + w * WPW;
+      const float* p = (const float*)vec + col0;
 #pragma unroll
       for (int i = 0; i < WPW / 4; ++i) {
         f32x4 t = *(const f32x4_a4*)(p + 4 * i);
@@ -236,59 +258,91 @@ __device__ __forceinline__ void prep_x(XRegs<BITS, V, SPLIT>& X, const void* vec
   }
 }
 
-// Scales a lane needs for one row: its V words touch groups g0 .. g0+NS-1.
+// Scales a lane needs for one row. A 4-word chunk never straddles a scale
+// group (a group is 8 words for Q4, 4 for Q2, and chunks are 4-aligned), so
+// each chunk takes one scale; a 3-word tail may straddle two groups, the
+// others take one.
 template <int BITS, int V>
 struct ScalePlan {
   static constexpr int WPG = QT<BITS>::WPG;
-  static constexpr bool ALIGNED = (V % WPG) == 0;  // lane starts a group
-  static constexpr bool WITHIN = (WPG % V) == 0;   // lane inside one group
-  static constexpr int NS = ALIGNED ? V / WPG : (WITHIN ? 1 : (V - 1) / WPG + 2);
+  static constexpr int N4 = LaneMap<V>::N4;
+  static constexpr int R = LaneMap<V>::R;
+  static constexpr int NT = R == 3 ? 2 : (R > 0 ? 1 : 0);
+  static constexpr int NS = N4 + NT;
 };
 
-// Sum over the lane's words of scale(word) * (dot - K), for one row.
-template <int BITS, int V, bool SPLIT, typename ST>
+// Group index of each of the lane's scales, and (tmask) which tail words sit
+// in the tail's second group.
+template <int BITS, int V>
+__device__ __forceinline__ void scale_groups(int lr, int LPR, int (&g)[ScalePlan<BITS, V>::NS],
+                                             int& tmask) {
+  using SP = ScalePlan<BITS, V>;
+  using LM = LaneMap<V>;
+#pragma unroll
+  for (int c = 0; c < SP::N4; ++c) g[c] = LM::word(lr, LPR, 4 * c) / SP::WPG;
+  tmask = 0;
+  if constexpr (SP::R > 0) {
+    const int gt = LM::word(lr, LPR, 4 * SP::N4) / SP::WPG;
+    g[SP::N4] = gt;
+    if constexpr (SP::NT == 2) g[SP::N4 + 1] = gt + 1;
+#pragma unroll
+    for (int t = 0; t < SP::R; ++t)
+      if (LM::word(lr, LPR, 4 * SP::N4 + t) / SP::WPG != gt) tmask |= 1 << t;
+  }
+}
+
+template <int BITS, int V, typename ST, bool NT>
+__device__ __forceinline__ void load_row_scales(const ST* __restrict__ row_scales,
+                                                const int (&g)[ScalePlan<BITS, V>::NS], int G,
+                                                float (&s)[ScalePlan<BITS, V>::NS]) {
+#pragma unroll
+  for (int j = 0; j < ScalePlan<BITS, V>::NS; ++j)
+    s[j] = load_scale<ST, NT>(row_scales + (g[j] < G ? g[j] : G - 1));
+}
+
+// Fold the per-word offsets to one per scale: K[c] = sum over chunk c's four
+// words, then the tail words' own offsets. Call once after the pairs are built.
+template <int BITS, int V, bool SPLIT>
+__device__ __forceinline__ void fold_k(XRegs<BITS, V, SPLIT>& X) {
+  using SP = ScalePlan<BITS, V>;
+#pragma unroll
+  for (int c = 0; c < SP::N4; ++c)
+    X.K[c] = X.K[4 * c] + X.K[4 * c + 1] + X.K[4 * c + 2] + X.K[4 * c + 3];
+#pragma unroll
+  for (int t = 0; t < SP::R; ++t) X.K[SP::N4 + t] = X.K[4 * SP::N4 + t];
+}
+
+// Sum over the lane's words of scale(word) * (dot - K), for one row (K folded).
+template <int BITS, int V, bool SPLIT>
 __device__ __forceinline__ float lane_row(const uint32_t (&cw)[V], const XRegs<BITS, V, SPLIT>& X,
-                                          const float (&s)[ScalePlan<BITS, V>::NS],
-                                          const int (&slot)[V]) {
+                                          const float (&s)[ScalePlan<BITS, V>::NS], int tmask) {
   using SP = ScalePlan<BITS, V>;
   float acc = 0.f;
-  if constexpr (SP::ALIGNED || SP::WITHIN) {
-    constexpr int WG = SP::ALIGNED ? SP::WPG : V;  // words sharing one scale
 #pragma unroll
-    for (int g = 0; g < SP::NS; ++g) {
-      float kk = 0.f;
+  for (int c = 0; c < SP::N4; ++c) {
+    float a = -X.K[c];
 #pragma unroll
-      for (int w = g * WG; w < (g + 1) * WG; ++w) kk += X.K[w];
-      float a = -kk;
-#pragma unroll
-      for (int w = g * WG; w < (g + 1) * WG; ++w) {
-        a = dot_word<BITS>(cw[w], X.hi[w], a);
-        if constexpr (SPLIT) a = dot_word<BITS>(cw[w], X.lo[w], a);
-      }
-      acc = fmaf(a, s[g], acc);
-    }
-  } else {
-#pragma unroll
-    for (int w = 0; w < V; ++w) {
-      float a = dot_word<BITS>(cw[w], X.hi[w], -X.K[w]);
+    for (int w = 4 * c; w < 4 * c + 4; ++w) {
+      a = dot_word<BITS>(cw[w], X.hi[w], a);
       if constexpr (SPLIT) a = dot_word<BITS>(cw[w], X.lo[w], a);
-      float sc = s[0];
+    }
+    acc = fmaf(a, s[c], acc);
+  }
+  if constexpr (SP::R > 0) {
+    // the tail's scale(s) as opaque register values, so the per-word choice
+    // stays a register select (not an indexed load from a stack copy)
+    float t0 = s[SP::N4], t1 = s[SP::NS - 1];
+    asm volatile("" : "+v"(t0), "+v"(t1));
 #pragma unroll
-      for (int j = 1; j < SP::NS; ++j) sc = slot[w] >= j ? s[j] : sc;
+    for (int t = 0; t < SP::R; ++t) {
+      const int w = 4 * SP::N4 + t;
+      float a = dot_word<BITS>(cw[w], X.hi[w], -X.K[SP::N4 + t]);
+      if constexpr (SPLIT) a = dot_word<BITS>(cw[w], X.lo[w], a);
+      const float sc = (SP::NT == 2 && ((tmask >> t) & 1)) ? t1 : t0;
       acc = fmaf(a, sc, acc);
     }
   }
   return acc;
-}
-
-template <int BITS, int V, typename ST>
-__device__ __forceinline__ void load_scales(const ST* __restrict__ row_scales, int g0, int G,
-                                            float (&s)[ScalePlan<BITS, V>::NS]) {
-#pragma unroll
-  for (int j = 0; j < ScalePlan<BITS, V>::NS; ++j) {
-    const int g = g0 + j < G ? g0 + j : G - 1;
-    s[j] = load_scale(row_scales + g);
-  }
 }
 
 }  // namespace smoe

@@ -6,14 +6,6 @@
 
 namespace smoe {
 
-template <int BITS, int V>
-__device__ __forceinline__ void scale_slots(int lr, int (&slot)[V], int& g0) {
-  constexpr int WPG = QT<BITS>::WPG;
-  g0 = (lr * V) / WPG;
-#pragma unroll
-  for (int w = 0; w < V; ++w) slot[w] = (lr * V + w) / WPG - g0;
-}
-
 // gate/up + SwiGLU: h[p, r] = silu(gate_r . x) * (up_r . x)
 template <int BITS, int V, typename ST, bool BF16>
 __global__ __launch_bounds__(256) void k_gate_up(GemvArgs A) {
@@ -39,29 +31,30 @@ __global__ __launch_bounds__(256) void k_gate_up(GemvArgs A) {
             RPW = 64 >> lg;
   const int Wr = A.m0.words_per_row, G = A.m0.cols / 64;
   const uint8_t* blob = A.blobs + (uint64_t)e * A.stride;
-  const uint32_t* gcodes = (const uint32_t*)(blob + A.m0.codes_off) + lr * V;
-  const uint32_t* ucodes = (const uint32_t*)(blob + A.m1.codes_off) + lr * V;
+  const uint32_t* gcodes = (const uint32_t*)(blob + A.m0.codes_off);
+  const uint32_t* ucodes = (const uint32_t*)(blob + A.m1.codes_off);
   const ST* gsc = (const ST*)(blob + A.m0.scales_off);
   const ST* usc = (const ST*)(blob + A.m1.scales_off);
-  int slot[V], g0;
-  scale_slots<BITS, V>(lr, slot, g0);
+  int sg[SP::NS], tmask;
+  scale_groups<BITS, V>(lr, LPR, sg, tmask);
   for (int p = p0; p < p1; ++p) {
     const int t = A.shared ? p : A.pair_token[p];
     XRegs<BITS, V, SPLIT> X;
     const void* xv = BF16 ? (const void*)((const uint16_t*)A.x + (size_t)t * A.x_ld)
                           : (const void*)((const float*)A.x + (size_t)t * A.x_ld);
     prep_x<BITS, V, SPLIT, BF16>(X, xv, lr, lg, A.rms != 0, A.eps, A.m0.cols);
+    fold_k(X);
     for (int rb = row0; rb < row1; rb += RPW) {
       const int r = rb + rsub;
       const int rc = r < rows ? r : rows - 1;
       uint32_t gw[V], uw[V];
-      load_words<V>(gcodes + (size_t)rc * Wr, gw);
-      load_words<V>(ucodes + (size_t)rc * Wr, uw);
+      load_row_words<V, false>(gcodes + (size_t)rc * Wr, lr, LPR, gw);
+      load_row_words<V, false>(ucodes + (size_t)rc * Wr, lr, LPR, uw);
       float gs[SP::NS], us[SP::NS];
-      load_scales<BITS, V, ST>(gsc + (size_t)rc * G, g0, G, gs);
-      load_scales<BITS, V, ST>(usc + (size_t)rc * G, g0, G, us);
-      float ag = lane_row<BITS, V, SPLIT, ST>(gw, X, gs, slot);
-      float au = lane_row<BITS, V, SPLIT, ST>(uw, X, us, slot);
+      load_row_scales<BITS, V, ST, false>(gsc + (size_t)rc * G, sg, G, gs);
+      load_row_scales<BITS, V, ST, false>(usc + (size_t)rc * G, sg, G, us);
+      float ag = lane_row<BITS, V, SPLIT>(gw, X, gs, tmask);
+      float au = lane_row<BITS, V, SPLIT>(uw, X, us, tmask);
       ag = seg_sum(ag, lg);
       au = seg_sum(au, lg);
       if (lr == LPR - 1 && r < row1) {
@@ -96,22 +89,23 @@ __global__ __launch_bounds__(256) void k_down(GemvArgs A) {
             RPW = 64 >> lg;
   const int Wr = A.m0.words_per_row, G = A.m0.cols / 64;
   const uint8_t* blob = A.blobs + (uint64_t)e * A.stride;
-  const uint32_t* codes = (const uint32_t*)(blob + A.m0.codes_off) + lr * V;
+  const uint32_t* codes = (const uint32_t*)(blob + A.m0.codes_off);
   const ST* sc = (const ST*)(blob + A.m0.scales_off);
-  int slot[V], g0;
-  scale_slots<BITS, V>(lr, slot, g0);
+  int sg[SP::NS], tmask;
+  scale_groups<BITS, V>(lr, LPR, sg, tmask);
   for (int p = p0; p < p1; ++p) {
     XRegs<BITS, V, SPLIT> X;
     prep_x<BITS, V, SPLIT, false>(X, (const float*)A.x + (size_t)p * A.x_ld, lr, lg, false,
                                   0.f, A.m0.cols);
+    fold_k(X);
     for (int rb = row0; rb < row1; rb += RPW) {
       const int r = rb + rsub;
       const int rc = r < rows ? r : rows - 1;
       uint32_t cw[V];
-      load_words<V>(codes + (size_t)rc * Wr, cw);
+      load_row_words<V, false>(codes + (size_t)rc * Wr, lr, LPR, cw);
       float s[SP::NS];
-      load_scales<BITS, V, ST>(sc + (size_t)rc * G, g0, G, s);
-      float a = lane_row<BITS, V, SPLIT, ST>(cw, X, s, slot);
+      load_row_scales<BITS, V, ST, false>(sc + (size_t)rc * G, sg, G, s);
+      float a = lane_row<BITS, V, SPLIT>(cw, X, s, tmask);
       a = seg_sum(a, lg);
       if (lr == LPR - 1 && r < row1) A.out[(size_t)p * rows + r] = a * X.oscale;
     }

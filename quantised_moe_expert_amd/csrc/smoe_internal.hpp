@@ -69,6 +69,13 @@ hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, i
                        const int* meta, const int* active, const int* offs, float* y,
                        hipStream_t stream);
 
+// Batch-1 path (two launches); sets *launched = false (and enqueues nothing)
+// when the layer's shape has no instantiation.
+hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, float eps,
+                       const float* logits, int k, int norm, float* out, int accumulate,
+                       int32_t* uids, float* uw, float* h, int32_t* ws_ids, float* ws_w,
+                       hipStream_t stream, bool* launched);
+
 hipError_t launch_combine(const float* y, const int* pair_of, const float* w,
                           const float* y_shared, float* out, int T, int k, int d,
                           int accumulate, hipStream_t stream);

@@ -100,6 +100,17 @@ SMALL = [
     (2048, 1408, 4, 2, 2, 4, "f32", False, 2816),
     (2048, 1408, 6, 3, 3, 2, "f16", True, 2816),
     (640, 448, 12, 5, 7, 4, "f32", True, 0),
+    # one token: the single-launch path for these widths ...
+    (512, 320, 16, 4, 1, 4, "f32", True, 0),
+    (512, 320, 16, 4, 1, 2, "f16", False, 0),
+    (2048, 1408, 64, 6, 1, 4, "f16", False, 0),
+    (2048, 1408, 64, 6, 1, 2, "f32", True, 0),
+    (4096, 1536, 128, 16, 1, 2, "f32", True, 0),
+    (4096, 1536, 512, 1, 1, 4, "f16", True, 0),
+    (256, 128, 4, 4, 1, 2, "f32", True, 0),
+    # ... and one-token shapes that take the multi-kernel path
+    (192, 64, 8, 8, 1, 4, "f16", True, 128),
+    (1024, 192, 32, 16, 1, 2, "f32", True, 0),
 ]
 
 
@@ -148,6 +159,56 @@ def test_repeat_calls_are_bitwise_identical():
     assert np.array_equal(a, b)
 
 
+def test_single_token_repeated_launches_and_streams():
+    # the single-launch kernel's grid barrier must stay consistent across many
+    # launches, across layers, and across streams
+    torch = _torch()
+    hl = random_layer(21, 4096, 1536, 16, 4)
+    hl2 = random_layer(22, 4096, 1536, 16, 4)
+    dl, dl2 = DeviceLayer(hl), DeviceLayer(hl2)
+    r = synth.rng(23)
+    x = _x(r, 1, 4096, "bf16")
+    lgs = [synth.normal_f32(r, (1, 16)) for _ in range(3)]
+    ref = [O.moe_forward(hl.oracle(), x, lg, 8, True)[0] for lg in lgs]
+    ref2 = O.moe_forward(hl2.oracle(), x, lgs[0], 8, True)[0]
+    first = dl.forward(x, lgs[0], 8, True)[0]
+    assert rel_l2(first, ref[0]) <= TOL
+    for i in range(40):
+        out = dl.forward(x, lgs[i % 3], 8, True)[0]
+        assert rel_l2(out, ref[i % 3]) <= TOL, i
+        if i % 3 == 0:
+            assert np.array_equal(out, first)
+        if i % 5 == 0:
+            assert rel_l2(dl2.forward(x, lgs[0], 8, True)[0], ref2) <= TOL
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        out = dl.forward(x, lgs[1], 8, True)[0]
+    assert rel_l2(out, ref[1]) <= TOL
+
+
+def test_decode_step_multi_token_small():
+    torch = _torch()
+    import quantised_moe_expert_amd as smoe
+    hls = [random_layer(40 + l, 512, 320, 16, 4, "f16") for l in range(3)]
+    r = synth.rng(41)
+    T = 3
+    x = synth.normal_f32(r, (T, 512))
+    lg = synth.normal_f32(r, (3, T, 16))
+    dls = [DeviceLayer(h) for h in hls]
+    h_d = torch.from_numpy(x.copy()).cuda()
+    lg_d = torch.from_numpy(lg).cuda()
+    nws = smoe.smoe_workspace_bytes(dls[0].handle, T, 4)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    smoe.smoe_decode_step([d.handle for d in dls], h_d.data_ptr(), lg_d.data_ptr(), T, 4, False,
+                          1e-6, ws.data_ptr(), nws, 0)
+    torch.cuda.synchronize()
+    got = h_d.cpu().numpy()
+    ref = O.decode_step([h.oracle() for h in hls], x, list(lg), 4, False, 1e-6)
+    assert rel_l2(got - x, ref - x) <= TOL
+    for t in range(T):
+        assert rel_l2(got[t] - x[t], ref[t] - x[t]) <= TOL
+
+
 def test_activation_range_is_scale_free():
     # outputs scale linearly with x; the per-vector power-of-two rescale keeps
     # fp16 in range for large and tiny activations
@@ -162,6 +223,8 @@ def test_activation_range_is_scale_free():
         out = dl.forward(xs, lg, 2, True, "f32")[0]
         ref = O.moe_forward(hl.oracle(), xs, lg, 2, True)[0]
         assert rel_l2(out, ref) <= TOL
+        out1 = dl.forward(xs[:1], lg[:1], 2, True, "f32")[0]
+        assert rel_l2(out1, ref[:1]) <= TOL
 
 
 # ------------------------------------------------------------ the workloads --
