@@ -105,6 +105,14 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
   A.user_ids = uids;
   A.user_w = uw;
   A.rb = rb;
+  // routing split (see DecodeArgs): at most 32 lanes per expert, pairs per
+  // lane a multiple of 8, the padded key count within the LDS table
+  A.rk_kpw = (A.E + DEC_THREADS / 64 - 1) / (DEC_THREADS / 64);
+  A.rk_lg = 0;
+  while (A.rk_lg < 5 && (2 << A.rk_lg) * A.rk_kpw <= 64) ++A.rk_lg;
+  A.rk_cp = ((A.E + 1) / 2 + (1 << A.rk_lg) - 1) >> A.rk_lg;
+  A.rk_cp = (A.rk_cp + 7) / 8 * 8;
+  if ((2 * A.rk_cp << A.rk_lg) > DEC_KEYS) return hipSuccess;
   hipError_t e = gu(A, DEC_NWG, stream);
   if (e != hipSuccess) return e;
   e = dn(A, DEC_NWG, stream);

@@ -35,10 +35,15 @@ namespace smoe {
 
 constexpr int DEC_WAVES = DEC_THREADS / 64;
 
-// Order-preserving map of a float (with -0 folded to +0) to a signed int.
-__device__ __forceinline__ int ordered_key(float f) {
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+// Routing key of expert e with logit f: unsigned order of the keys is the
+// selection order (larger logit first, -0 equal to +0, equal logits in
+// ascending id); every key is distinct and above 0, the padding key.
+__device__ __forceinline__ uint64_t route_key(float f, int e) {
   const int b = __builtin_bit_cast(int, f + 0.0f);
-  return b >= 0 ? b : b ^ 0x7FFFFFFF;
+  const uint32_t o = (uint32_t)(b >= 0 ? b : b ^ 0x7FFFFFFF) ^ 0x80000000u;
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
 // Power-of-two factor that brings a vector whose largest magnitude is amax to
@@ -84,16 +89,22 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_gate_up(DecodeArgs A) {
   constexpr int NPOS = QT<BITS>::NPOS;
   constexpr bool SPLIT = XF32;
   using SPG = ScalePlan<BITS, VG>;
-  // units per batch; two batches are in flight (double buffering)
-  constexpr int UBr = (SPLIT ? 36 : 48) / (2 * (VG + SPG::NS));
+  // units per batch; two batches are in flight (double buffering). More
+  // loads in flight per wave measured slower: the first batch then arrives
+  // later and the memory queues hold more concurrent row streams.
+#ifdef SMOE_DEC_UB
+  constexpr int UB = SMOE_DEC_UB;
+#else
+  constexpr int UBr = (SPLIT ? 36 : 24) / (2 * (VG + SPG::NS));
   constexpr int UB = UBr < 1 ? 1 : (UBr > 4 ? 4 : UBr);
+#endif
   constexpr int XP = VG * PPW * 64;
   constexpr int XRAW = XF32 ? WPW : WPW / 2;  // 32-bit words of x per code word
 
   __shared__ uint32_t s_xp[(SPLIT ? 2 : 1) * XP];
   __shared__ float s_K[VG * 64];
-  __shared__ __attribute__((aligned(16))) int s_key[SMOE_MAX_EXPERTS + 4];
-  __shared__ int s_rank[SMOE_MAX_EXPERTS];
+  __shared__ __attribute__((aligned(16))) uint64_t s_key[DEC_KEYS];
+  __shared__ float s_lv[SMOE_MAX_EXPERTS];
   __shared__ int s_ids[SMOE_MAX_TOP_K];
   __shared__ float s_val[SMOE_MAX_TOP_K];
   __shared__ float s_tmp[DEC_WAVES];
@@ -106,11 +117,13 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_gate_up(DecodeArgs A) {
   // 1. loads: the x words this thread turns into fp16 pairs, and one logit
   const int Wg = A.d * BITS / 32;
   uint32_t xraw[DEC_XW][XRAW];
+  // slot t is used when t * DEC_THREADS < Wg (a workgroup-uniform test); the
+  // threads past Wg in the last slot load a valid word and ignore it
 #pragma unroll
   for (int t = 0; t < DEC_XW; ++t) {
     const int cw = tid + t * DEC_THREADS;
-    if (cw < Wg) {
-      const uint32_t* src = (const uint32_t*)A.x + (size_t)cw * XRAW;
+    if (t * DEC_THREADS < Wg) {
+      const uint32_t* src = (const uint32_t*)A.x + (size_t)(cw < Wg ? cw : Wg - 1) * XRAW;
 #pragma unroll
       for (int c = 0; c < XRAW / 4; ++c) {
         const u32x4 v = *(const u32x4*)(src + 4 * c);
@@ -122,22 +135,27 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_gate_up(DecodeArgs A) {
     }
   }
   float lv = -INFINITY;
+  const int nkeys = 2 * A.rk_cp << A.rk_lg;
   if (tid < E) {
     lv = A.logits[tid];
     if (lv != lv) lv = -INFINITY;  // NaN never outranks a number
-    s_key[tid] = ordered_key(lv);
-    s_rank[tid] = 0;
-  } else if (tid < E + 4) {
-    s_key[tid] = (int)0x80000000;  // padding read by the vector loop below
+    s_lv[tid] = lv;
+    s_key[tid] = route_key(lv, tid);
   }
+  for (int e = E + tid; e < nkeys; e += DEC_THREADS) s_key[e] = 0;
+  // one explicit wait for all of these loads in straight-line code: waits
+  // inserted inside the conditional blocks below would leave xraw "pending"
+  // at their joins, and the compiler would then wait for every outstanding
+  // load (the first weight batch included) where the pairs are built
+  __builtin_amdgcn_s_waitcnt(0);
   float amax = 0.f, ssq = 0.f;
 #pragma unroll
   for (int t = 0; t < DEC_XW; ++t) {
     const int cw = tid + t * DEC_THREADS;
-    if (cw < Wg) {
+    if (t * DEC_THREADS < Wg) {
 #pragma unroll
       for (int i = 0; i < WPW; ++i) {
-        const float f = x_word_val<XF32>(xraw[t], i);
+        const float f = cw < Wg ? x_word_val<XF32>(xraw[t], i) : 0.f;
         amax = fmaxf(amax, fabsf(f));
         ssq = fmaf(f, f, ssq);
       }
@@ -151,34 +169,29 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_gate_up(DecodeArgs A) {
   }
   __syncthreads();
 
-  // 2. routing: rank of logit i = number of logits ahead of it (larger, or
-  //    equal with a lower id); thread t counts one slice of the keys
+  // 2. routing: the rank of expert i is the number of keys above its own;
+  //    2^rk_lg adjacent lanes share expert i, lane part p of them compares
+  //    against key pairs p, p + 2^rk_lg, ... (distinct LDS banks per part),
+  //    and the ranks below k place the expert in the selection
   {
-    const int parts = DEC_THREADS / E;  // >= 1
-    if (tid < parts * E) {
-      const int i = tid % E, part = tid / E;
-      const int lo = part * E / parts, hi = (part + 1) * E / parts;
-      const int ki = s_key[i];
-      int cnt = 0;
-      for (int e = lo & ~3; e < hi; e += 4) {
-        const int4 kv = *(const int4*)(s_key + e);
-        const int ks[4] = {kv.x, kv.y, kv.z, kv.w};
+    const int lg = A.rk_lg, lpk = 1 << lg;
+    const int kl = lane >> lg, part = lane & (lpk - 1);
+    const int i = wave * A.rk_kpw + kl;
+    const bool mine = kl < A.rk_kpw && i < E;
+    const uint64_t ki = s_key[mine ? i : 0];
+    const u64x2* kp = (const u64x2*)s_key + part;
+    int cnt = 0;
+    for (int c = 0; c < A.rk_cp; c += 8) {
+      u64x2 v[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ee = e + q;
-          const bool ahead = (ks[q] > ki) | ((ks[q] == ki) & (ee < i));
-          cnt += (ee >= lo) & (ee < hi) & ahead;
-        }
-      }
-      atomicAdd(&s_rank[i], cnt);
+      for (int u = 0; u < 8; ++u) v[u] = kp[(c + u) << lg];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cnt += (int)(v[u].x > ki) + (int)(v[u].y > ki);
     }
-  }
-  __syncthreads();
-  if (tid < E) {
-    const int r = s_rank[tid];
-    if (r < k) {
-      s_ids[r] = tid;
-      s_val[r] = lv;
+    const int r = (int)seg_sum((float)cnt, lg);
+    if (mine && part == lpk - 1 && r < k) {
+      s_ids[r] = i;
+      s_val[r] = s_lv[i];
     }
   }
   __syncthreads();
@@ -225,8 +238,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_gate_up(DecodeArgs A) {
   Batch bA, bB;
   if (my_n > 0) issue_b(bA, 0);
 
-  // 4. while those loads are in flight: fp16 activation pairs (once per
-  //    workgroup) and the routing weights
+  // 4. while the first batch is in flight: fp16 activation pairs and
+  //    offsets K, once per workgroup, into LDS
   float S, xos;
   {
     float m = 0.f, q = 0.f;
@@ -242,7 +255,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_gate_up(DecodeArgs A) {
 #pragma unroll
   for (int t = 0; t < DEC_XW; ++t) {
     const int cw = tid + t * DEC_THREADS;
-    if (cw < Wg) {
+    if (t * DEC_THREADS < Wg && cw < Wg) {
       // lane lr and slot w holding code word cw (inverse of LaneMap)
       constexpr int N4 = LaneMap<VG>::N4, RT = LaneMap<VG>::R;
       int lr, w;
@@ -275,6 +288,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_gate_up(DecodeArgs A) {
       s_K[w * LPRG + lr] = kk;
     }
   }
+
   if (blockIdx.x == 0) {
     // softmax over all logits (only the publishing workgroup needs weights)
     const float mx = s_val[0];
@@ -343,8 +357,13 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_down(DecodeArgs A) {
   constexpr int WPW = QT<BITS>::WPW;
   constexpr int NPOS = QT<BITS>::NPOS;
   using SPD = ScalePlan<BITS, VD>;
+  // row loads per batch, two batches in flight
+#ifdef SMOE_DEC_UD
+  constexpr int UD = SMOE_DEC_UD;
+#else
   constexpr int UDr = 32 / (VD + SPD::NS);
-  constexpr int UD = UDr < 1 ? 1 : (UDr > 8 ? 8 : UDr);  // row loads per batch (x2 in flight)
+  constexpr int UD = UDr < 1 ? 1 : (UDr > 8 ? 8 : UDr);
+#endif
 
   __shared__ float s_part[SMOE_MAX_TOP_K * DEC_RB_MAX];
 

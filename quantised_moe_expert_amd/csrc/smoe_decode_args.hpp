@@ -1,5 +1,5 @@
-// Argument block and launcher declarations of the single-launch batch-1
-// layer kernel (see smoe_decode.hpp).
+// Argument block and launcher declarations of the two-launch batch-1 layer
+// kernels (see smoe_decode.hpp).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,6 +16,7 @@ constexpr int DEC_XW = 4;          // x code words per thread (d * bits / 32 <= 
 constexpr int DEC_HJ = 2;          // h vectors staged per wave (k <= 16)
 constexpr int DEC_HC = 4;          // h code words per lane (Q4; half for Q2)
 constexpr int DEC_H_LDS = 12288;   // fp16 pairs of h held in LDS (k * ffn / 2 <= 12288)
+constexpr int DEC_KEYS = 512;      // routing keys in LDS, padding included
 
 struct DecodeArgs {
   const uint8_t* blobs;  // routed expert bank, expert e at blobs + e * stride
@@ -35,6 +36,9 @@ struct DecodeArgs {
   int32_t* user_ids;     // optional [k]
   float* user_w;         // optional [k]
   int rb;                // down rows per workgroup
+  // routing split: wave w ranks experts [w * rk_kpw, (w + 1) * rk_kpw), with
+  // 2^rk_lg lanes per expert, each comparing against rk_cp key pairs
+  int rk_kpw, rk_lg, rk_cp;
 };
 
 template <int BITS, typename ST, int VG, bool XF32>

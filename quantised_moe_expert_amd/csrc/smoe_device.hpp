@@ -145,6 +145,16 @@ __device__ __forceinline__ float load_scale(const ST* p) {
   return NT ? (float)__builtin_nontemporal_load(p) : (float)*p;
 }
 
+// (v & mask) | magic as one v_and_or_b32. A VOP3 instruction on gfx9-class
+// targets takes no literal and reads at most one SGPR, so the mask comes in an
+// SGPR and the magic in a VGPR; written as plain C the pair compiles to two
+// VOP2 instructions with literals.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(magic));
+  return r;
+}
+
 // Sum over one code word of (code_i - m) * x_i (up to the K offset, which the
 // caller folds into acc): see the file comment.
 template <int BITS>
@@ -157,7 +167,7 @@ __device__ __forceinline__ float dot_word(uint32_t w, const f16x2* xp, float acc
     for (int pos = 0; pos < NPOS; ++pos) {
       constexpr uint32_t base = (1u << BITS) - 1u;
       const uint32_t m = (base << (BITS * pos)) | (base << (BITS * pos + 16));
-      acc = fdot2((v & m) | 0x64006400u, xp[hs * NPOS + pos], acc);
+      acc = fdot2(and_or(v, m, 0x64006400u), xp[hs * NPOS + pos], acc);
     }
   }
   return acc;
