@@ -41,6 +41,11 @@ def parse():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--trace-launches", type=int, default=400,
+                    help="forwards per kernel in the per-launch timing pass (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -50,6 +55,9 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
               "sharding is described in the design notes but not implemented", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import numpy as np
     import torch
     import synth
@@ -110,11 +118,12 @@ def main():
     nws = smoe.smoe_workspace_bytes(handles[0], T, k)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
 
-    # unique experts each step reads (algorithmic bytes)
+    # unique experts each step reads (algorithmic bytes); uniq0: layer 0 only
     top = torch.topk(lg_sets, k, dim=-1).indices  # [S, L, T, k]
-    uniq = []
+    uniq, uniq0 = [], []
     for s in range(n_logit_sets):
         uniq.append(sum(int(torch.unique(top[s, l]).numel()) for l in range(W.n_layers)))
+        uniq0.append(int(torch.unique(top[s, 0]).numel()))
     shared_raw = 0
     if W.shared_ffn_dim:
         shared_raw = smoe.smoe_expert_layout_of(W.d_model, W.shared_ffn_dim, W.bits,
@@ -158,10 +167,51 @@ def main():
     pairs = T * k * W.n_layers
     avg_unique = sum(uniq[(args.warmup + i) % n_logit_sets] for i in range(args.steps)) / args.steps
 
+    # per-launch timing of the two expert kernels: HIP events recorded by the
+    # library immediately around the launch, on the launch's stream, one pair
+    # per forward, in a pass of its own after the timed loop
     single = T == 1 and not W.shared_ffn_dim and os.environ.get("SMOE_FORCE_MULTI_KERNEL") != "1"
-    kernel_label = ("k_decode1: one launch per layer (events around the timed loop of "
-                    "back-to-back launches)" if single else
-                    "whole forward (route, gate/up, down, combine launches)")
+    x_bytes = T * W.d_model * (2 if W.x_dtype == "bf16" else 4)
+    gu_raw = sum(t.codes_bytes + t.scales_bytes for t in (lay.gate, lay.up))
+    dn_raw = lay.down.codes_bytes + lay.down.scales_bytes
+    h_bytes = T * k * W.ffn_dim * 4
+    start = args.warmup + args.steps
+    kern = {}
+    if args.trace_launches > 0:
+        for name, kid in (("gate_up", smoe.SMOE_KERNEL_GATE_UP), ("down", smoe.SMOE_KERNEL_DOWN)):
+            n = args.trace_launches
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+            for a, b in evs:  # creates the events
+                a.record(stream)
+                b.record(stream)
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(evs):
+                smoe.smoe_trace_kernel(kid, int(a.cuda_event), int(b.cuda_event))
+                step(start + i)
+            torch.cuda.synchronize()
+            smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_NONE)
+            dts = [a.elapsed_time(b) * 1e-3 for a, b in evs]  # s
+            u = [uniq0[(start + i) % n_logit_sets] for i in range(n)]
+            if name == "gate_up":
+                byts = [ui * gu_raw + x_bytes + T * E * 4 + h_bytes for ui in u]
+            else:
+                out_b = T * W.d_model * 4 * (2 if stack else 1)  # read-modify-write in a stack
+                byts = [ui * dn_raw + h_bytes + out_b if single else
+                        ui * dn_raw + h_bytes + T * k * W.d_model * 4 for ui in u]
+            mean_dt = sum(dts) / n
+            mean_b = sum(byts) / n
+            kern[name] = {"mean_us": mean_dt * 1e6, "median_us": sorted(dts)[n // 2] * 1e6,
+                          "bytes": mean_b, "GBps": mean_b / mean_dt / 1e9}
+            start += n
+    if single:
+        names = {"gate_up": "k_dec_gate_up (routing + gate/up + SwiGLU, one launch per layer)",
+                 "down": "k_dec_down (down projection + weighted combine)"}
+    else:
+        names = {"gate_up": "k_gate_up (grouped gate/up + SwiGLU over the routed pairs)",
+                 "down": "k_down (grouped down projection)"}
+    dom = kern.get("gate_up")
+    traffic = committed_traffic(W.name, "gate_up" if single else "gate_up_grouped")
     result = {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
@@ -187,16 +237,23 @@ def main():
         "expert_reads_per_s": round(avg_unique / (ms * 1e-3), 1),
         "pairs_per_s": round(pairs / (ms * 1e-3), 1),
         "wall_s_timed": round(t_wall, 3),
+        "algorithmic_bytes_per_step": int(alg_bytes),
         "roofline": {
             "bound": "hbm",
-            "kernel": kernel_label,
-            "achieved": round(achieved, 1),
+            "kernel": names["gate_up"],
+            "achieved": round(dom["GBps"], 1) if dom else None,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
-            "algorithmic_bytes_per_step": int(alg_bytes),
+            "frac": round(dom["GBps"] / HBM_PEAK_GBPS, 4) if dom else None,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(dom["bytes"]) if dom else None,
+            "launch_us_mean": round(dom["mean_us"], 3) if dom else None,
+            "launch_us_median": round(dom["median_us"], 3) if dom else None,
+            "launches_timed": args.trace_launches,
         },
+        "kernels": {names[n]: {"launch_us_mean": round(v["mean_us"], 3),
+                               "algorithmic_bytes_per_launch": int(v["bytes"]),
+                               "GBps": round(v["GBps"], 1)} for n, v in kern.items()},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, W, banks[0], stride, lg_sets[0, 0], x,
@@ -204,6 +261,55 @@ def main():
     print(json.dumps(result), flush=True)
     for h in handles:
         smoe.smoe_free(h)
+
+
+KERNEL_SOURCES = {
+    "gate_up": ("smoe_decode.hpp", "smoe_decode_args.hpp", "smoe_device.hpp"),
+    "gate_up_grouped": ("smoe_gemv.hpp", "smoe_gemv_args.hpp", "smoe_device.hpp"),
+}
+
+
+def kernel_sources_digest(kernel: str) -> str:
+    """sha256 over the device sources of a kernel, so a committed counter
+    reading can be matched to the code it was taken on."""
+    import hashlib
+    d = os.path.join(ROOT, "quantised_moe_expert_amd", "csrc")
+    hsh = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(d, f), "rb") as fh:
+            hsh.update(f.encode() + b"\0" + fh.read())
+    return hsh.hexdigest()[:16]
+
+
+def committed_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (profiles/traffic.txt: FETCH_SIZE + WRITE_SIZE per dispatch, scaled
+    by the plain-copy calibration), or None when there is none for this
+    workload and kernel or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_sources_digest(kernel)
+    with open(path) as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) == 4 and f[0] == workload and f[1] == kernel and f[2] == digest:
+                return float(f[3])
+    return None
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, five times: under rocprofv3
+    --pmc its FETCH_SIZE / WRITE_SIZE per dispatch, divided by 1 GiB, are the
+    counters' scale factors."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "copies": 5}), flush=True)
 
 
 def cpu_baseline(args, W, bank, stride, logits, x, shared_blob):

@@ -195,6 +195,26 @@ int smoe_decode_step(const smoe_layer* const* layers, int n_layers, float* d_h,
                      const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
                      float eps, void* d_workspace, uint64_t ws_bytes, void* hip_stream);
 
+/* Kernel timing hook (instrumentation for benchmarks; not an operation of
+ * the pages). Arms a one-shot pair of HIP events: the next smoe_moe_forward
+ * or smoe_decode_step call that launches the chosen kernel attaches them to
+ * that launch as its start and stop events (hipExtLaunchKernel), so their
+ * elapsed time is the kernel's own execution, then disarms.
+ *  kernel  SMOE_KERNEL_GATE_UP: the routed experts' gate/up + SwiGLU launch
+ *          (on the one-token path this launch also routes);
+ *          SMOE_KERNEL_DOWN: the routed experts' down-projection launch (on
+ *          the one-token path it also combines);
+ *          SMOE_KERNEL_NONE: disarm.
+ *  hip_event_before, hip_event_after  hipEvent_t values created and owned by
+ *          the caller (timing enabled); read them with hipEventElapsedTime
+ *          after synchronising.
+ * The armed pair is process-wide, not per thread or stream.
+ * Errors: SMOE_E_ARG for an unknown kernel or a null event when arming. */
+#define SMOE_KERNEL_NONE 0
+#define SMOE_KERNEL_GATE_UP 1
+#define SMOE_KERNEL_DOWN 2
+int smoe_trace_kernel(int kernel, void* hip_event_before, void* hip_event_after);
+
 #ifdef __cplusplus
 }
 #endif

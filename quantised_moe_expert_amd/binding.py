@@ -34,11 +34,15 @@ SMOE_MAX_TOP_K = 16
 SMOE_MAX_EXPERTS = 512
 SMOE_MAX_TOKENS = 1024
 
+SMOE_KERNEL_NONE = 0
+SMOE_KERNEL_GATE_UP = 1
+SMOE_KERNEL_DOWN = 2
+
 # every symbol include/smoe.h declares
 EXPORTED = (
     "smoe_version", "smoe_last_error", "smoe_expert_layout_of", "smoe_load_blobs",
     "smoe_free", "smoe_workspace_bytes", "smoe_route", "smoe_moe_forward",
-    "smoe_decode_step",
+    "smoe_decode_step", "smoe_trace_kernel",
 )
 
 
@@ -123,6 +127,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.smoe_decode_step.restype = _I
     lib.smoe_decode_step.argtypes = [ctypes.POINTER(_P), _I, _P, _P, _I, _I, _I,
                                      ctypes.c_float, _P, _U64, _P]
+    lib.smoe_trace_kernel.restype = _I
+    lib.smoe_trace_kernel.argtypes = [_I, _P, _P]
     if path is None:
         _lib = lib
     return lib
@@ -199,3 +205,8 @@ def smoe_decode_step(layers: Sequence[int], d_h: int, d_logits: int, n_tokens: i
                                            n_tokens, top_k, int(bool(norm_topk_prob)),
                                            float(eps), d_workspace or None, ws_bytes,
                                            hip_stream or None))
+
+
+def smoe_trace_kernel(kernel: int, hip_event_before: int = 0, hip_event_after: int = 0) -> None:
+    _check(load_library().smoe_trace_kernel(kernel, hip_event_before or None,
+                                            hip_event_after or None))

@@ -10,9 +10,11 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "smoe_internal.hpp"
+#include "smoe_launch.hpp"
 
 struct smoe_layer {
   smoe::LayerInfo info;
@@ -121,6 +123,11 @@ WsLayout ws_layout(const LayerInfo& L, int T, int k) {
   return W;
 }
 
+// armed timing events (smoe_trace_kernel)
+std::mutex g_trace_mu;
+int g_trace_kernel = SMOE_KERNEL_NONE;
+hipEvent_t g_trace_before = nullptr, g_trace_after = nullptr;
+
 int check_hip(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SMOE_E_HIP, "%s: %s", what, hipGetErrorString(e));
   return SMOE_OK;
@@ -156,10 +163,13 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
                                    offs, pair_token, pair_of, s),
                       "route launch")))
     return rc;
-  if ((rc = check_hip(launch_gate_up(L, false, x, xmode, eps, T, max_slots, meta, active, offs,
-                                     pair_token, h, s),
-                      "gate/up launch")))
-    return rc;
+  {
+    TracedLaunch t(SMOE_KERNEL_GATE_UP);
+    rc = check_hip(launch_gate_up(L, false, x, xmode, eps, T, max_slots, meta, active, offs,
+                                  pair_token, h, s),
+                   "gate/up launch");
+  }
+  if (rc) return rc;
   float* ysh = nullptr;
   if (L.desc.shared_ffn_dim) {
     float* hsh = (float*)(ws + W.h_shared);
@@ -172,15 +182,30 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
                         "shared down launch")))
       return rc;
   }
-  if ((rc = check_hip(launch_down(L, false, h, T, max_slots, meta, active, offs, y, s),
-                      "down launch")))
-    return rc;
+  {
+    TracedLaunch t(SMOE_KERNEL_DOWN);
+    rc = check_hip(launch_down(L, false, h, T, max_slots, meta, active, offs, y, s),
+                   "down launch");
+  }
+  if (rc) return rc;
   return check_hip(
       launch_combine(y, pair_of, w, ysh, out, T, k, (int)L.desc.d_model, accumulate, s),
       "combine launch");
 }
 
 }  // namespace
+
+thread_local LaunchEvents t_launch_events;
+
+bool trace_take(int kernel, hipEvent_t* start, hipEvent_t* stop) {
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  if (g_trace_kernel != kernel) return false;
+  *start = g_trace_before;
+  *stop = g_trace_after;
+  g_trace_kernel = SMOE_KERNEL_NONE;
+  return true;
+}
+
 }  // namespace smoe
 
 using namespace smoe;
@@ -341,6 +366,18 @@ int smoe_decode_step(const smoe_layer* const* layers, int n_layers, float* d_h,
                           1, nullptr, nullptr, (uint8_t*)d_workspace, (hipStream_t)hip_stream);
     if (rc) return rc;
   }
+  return ok();
+}
+
+int smoe_trace_kernel(int kernel, void* hip_event_before, void* hip_event_after) {
+  if (kernel != SMOE_KERNEL_NONE && kernel != SMOE_KERNEL_GATE_UP && kernel != SMOE_KERNEL_DOWN)
+    return fail(SMOE_E_ARG, "unknown kernel id %d", kernel);
+  if (kernel != SMOE_KERNEL_NONE && (!hip_event_before || !hip_event_after))
+    return fail(SMOE_E_ARG, "null event");
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  g_trace_kernel = kernel;
+  g_trace_before = (hipEvent_t)hip_event_before;
+  g_trace_after = (hipEvent_t)hip_event_after;
   return ok();
 }
 

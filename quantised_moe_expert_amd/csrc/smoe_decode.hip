@@ -6,6 +6,7 @@
 
 #include "smoe_decode_args.hpp"
 #include "smoe_internal.hpp"
+#include "smoe_launch.hpp"
 
 namespace smoe {
 namespace {
@@ -113,9 +114,16 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
   A.rk_cp = ((A.E + 1) / 2 + (1 << A.rk_lg) - 1) >> A.rk_lg;
   A.rk_cp = (A.rk_cp + 7) / 8 * 8;
   if ((2 * A.rk_cp << A.rk_lg) > DEC_KEYS) return hipSuccess;
-  hipError_t e = gu(A, DEC_NWG, stream);
+  hipError_t e;
+  {
+    TracedLaunch t(SMOE_KERNEL_GATE_UP);
+    e = gu(A, DEC_NWG, stream);
+  }
   if (e != hipSuccess) return e;
-  e = dn(A, DEC_NWG, stream);
+  {
+    TracedLaunch t(SMOE_KERNEL_DOWN);
+    e = dn(A, DEC_NWG, stream);
+  }
   if (e != hipSuccess) return e;
   *launched = true;
   return hipSuccess;

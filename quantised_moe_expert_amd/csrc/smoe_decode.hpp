@@ -30,6 +30,7 @@
 
 #include "smoe_decode_args.hpp"
 #include "smoe_device.hpp"
+#include "smoe_launch.hpp"
 
 namespace smoe {
 
@@ -474,14 +475,12 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_down(DecodeArgs A) {
 
 template <int BITS, typename ST, int VG, bool XF32>
 hipError_t launch_dec_gate_up(const DecodeArgs& A, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_dec_gate_up<BITS, ST, VG, XF32>), dim3(nwg), dim3(DEC_THREADS), 0, s, A);
-  return hipGetLastError();
+  return launch_kernel(k_dec_gate_up<BITS, ST, VG, XF32>, dim3(nwg), dim3(DEC_THREADS), s, A);
 }
 
 template <int BITS, typename ST, int VD>
 hipError_t launch_dec_down(const DecodeArgs& A, int nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_dec_down<BITS, ST, VD>), dim3(nwg), dim3(DEC_THREADS), 0, s, A);
-  return hipGetLastError();
+  return launch_kernel(k_dec_down<BITS, ST, VD>, dim3(nwg), dim3(DEC_THREADS), s, A);
 }
 
 }  // namespace smoe

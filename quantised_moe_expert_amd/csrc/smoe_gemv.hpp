@@ -3,6 +3,7 @@
 
 #include "smoe_device.hpp"
 #include "smoe_gemv_args.hpp"
+#include "smoe_launch.hpp"
 
 namespace smoe {
 
@@ -116,17 +117,13 @@ __global__ __launch_bounds__(256) void k_down(GemvArgs A) {
 // Launchers, instantiated per (BITS, scale type, V) in smoe_gemv_inst.hip.
 template <int BITS, typename ST, int V>
 hipError_t launch_gu(const GemvArgs& A, bool bf16, dim3 grid, hipStream_t s) {
-  if (bf16)
-    hipLaunchKernelGGL((k_gate_up<BITS, V, ST, true>), grid, dim3(256), 0, s, A);
-  else
-    hipLaunchKernelGGL((k_gate_up<BITS, V, ST, false>), grid, dim3(256), 0, s, A);
-  return hipGetLastError();
+  return bf16 ? launch_kernel(k_gate_up<BITS, V, ST, true>, grid, dim3(256), s, A)
+              : launch_kernel(k_gate_up<BITS, V, ST, false>, grid, dim3(256), s, A);
 }
 
 template <int BITS, typename ST, int V>
 hipError_t launch_dn(const GemvArgs& A, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_down<BITS, V, ST, false>), grid, dim3(256), 0, s, A);
-  return hipGetLastError();
+  return launch_kernel(k_down<BITS, V, ST, false>, grid, dim3(256), s, A);
 }
 
 }  // namespace smoe

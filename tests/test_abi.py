@@ -181,3 +181,15 @@ def test_route_and_decode_argument_checks():
     finally:
         smoe.smoe_free(h)
         smoe.smoe_free(h2)
+
+
+def test_trace_kernel_argument_checks():
+    # arming validates the kernel id and the events; nothing is recorded
+    # until a forward launches the armed kernel, so fake handles are safe here
+    with pytest.raises(smoe.SmoeError) as e:
+        smoe.smoe_trace_kernel(7, FAKE, FAKE)
+    assert e.value.code == smoe.SMOE_E_ARG
+    with pytest.raises(smoe.SmoeError):
+        smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_GATE_UP, 0, FAKE)
+    smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_DOWN, FAKE, FAKE)
+    smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_NONE)  # disarm
