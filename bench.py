@@ -116,7 +116,7 @@ def main():
     h_state = torch.randn((T, W.d_model), device=dev, generator=gen) if stack else None
     out = torch.empty((T, W.d_model), dtype=torch.float32, device=dev)
     nws = smoe.smoe_workspace_bytes(handles[0], T, k)
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
 
     # unique experts each step reads (algorithmic bytes); uniq0: layer 0 only
     top = torch.topk(lg_sets, k, dim=-1).indices  # [S, L, T, k]
@@ -176,9 +176,23 @@ def main():
     dn_raw = lay.down.codes_bytes + lay.down.scales_bytes
     h_bytes = T * k * W.ffn_dim * 4
     start = args.warmup + args.steps
+    # does this layer have a separate down-projection launch?
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record(stream)
+    eb.record(stream)
+    torch.cuda.synchronize()
+    smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_DOWN, int(ea.cuda_event), int(eb.cuda_event))
+    step(start)
+    torch.cuda.synchronize()
+    separate_down = smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_NONE) == 0
+    start += 1
+    out_b = T * W.d_model * 4 * (2 if stack else 1)  # read-modify-write in a stack
     kern = {}
     if args.trace_launches > 0:
-        for name, kid in (("gate_up", smoe.SMOE_KERNEL_GATE_UP), ("down", smoe.SMOE_KERNEL_DOWN)):
+        passes = [("gate_up", smoe.SMOE_KERNEL_GATE_UP)]
+        if separate_down:
+            passes.append(("down", smoe.SMOE_KERNEL_DOWN))
+        for name, kid in passes:
             n = args.trace_launches
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(n)]
@@ -196,7 +210,6 @@ def main():
             if name == "gate_up":
                 byts = [ui * gu_raw + x_bytes + T * E * 4 + h_bytes for ui in u]
             else:
-                out_b = T * W.d_model * 4 * (2 if stack else 1)  # read-modify-write in a stack
                 byts = [ui * dn_raw + h_bytes + out_b if single else
                         ui * dn_raw + h_bytes + T * k * W.d_model * 4 for ui in u]
             mean_dt = sum(dts) / n
@@ -205,7 +218,7 @@ def main():
                           "bytes": mean_b, "GBps": mean_b / mean_dt / 1e9}
             start += n
     if single:
-        names = {"gate_up": "k_dec_gate_up (routing + gate/up + SwiGLU, one launch per layer)",
+        names = {"gate_up": "k_dec_gate_up (routing + gate/up + SwiGLU)",
                  "down": "k_dec_down (down projection + weighted combine)"}
     else:
         names = {"gate_up": "k_gate_up (grouped gate/up + SwiGLU over the routed pairs)",

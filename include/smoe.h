@@ -145,7 +145,8 @@ void smoe_free(smoe_layer* layer);
 
 /* Bytes of device workspace smoe_moe_forward needs for n_tokens tokens and
  * top_k (0 on invalid arguments). smoe_decode_step needs the same amount for
- * the largest layer it runs. */
+ * the largest layer it runs. Calls that share a workspace must be ordered
+ * (one stream, or synchronised). */
 uint64_t smoe_workspace_bytes(const smoe_layer* layer, int n_tokens, int top_k);
 
 /* Routing only ("CMF v2 Format Specification", 2.2):
@@ -209,6 +210,8 @@ int smoe_decode_step(const smoe_layer* const* layers, int n_layers, float* d_h,
  *          the caller (timing enabled); read them with hipEventElapsedTime
  *          after synchronising.
  * The armed pair is process-wide, not per thread or stream.
+ * Returns SMOE_OK when arming; when disarming, 1 if a pair was still armed
+ * (no such launch happened since) and 0 otherwise.
  * Errors: SMOE_E_ARG for an unknown kernel or a null event when arming. */
 #define SMOE_KERNEL_NONE 0
 #define SMOE_KERNEL_GATE_UP 1

@@ -207,6 +207,11 @@ def smoe_decode_step(layers: Sequence[int], d_h: int, d_logits: int, n_tokens: i
                                            hip_stream or None))
 
 
-def smoe_trace_kernel(kernel: int, hip_event_before: int = 0, hip_event_after: int = 0) -> None:
-    _check(load_library().smoe_trace_kernel(kernel, hip_event_before or None,
-                                            hip_event_after or None))
+def smoe_trace_kernel(kernel: int, hip_event_before: int = 0, hip_event_after: int = 0) -> int:
+    """Arm (or, with SMOE_KERNEL_NONE, disarm) the one-shot launch events;
+    disarming returns 1 when the armed pair never fired."""
+    rc = load_library().smoe_trace_kernel(kernel, hip_event_before or None,
+                                          hip_event_after or None)
+    if rc < 0:
+        raise SmoeError(rc, smoe_last_error())
+    return rc

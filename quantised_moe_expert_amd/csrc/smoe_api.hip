@@ -375,10 +375,11 @@ int smoe_trace_kernel(int kernel, void* hip_event_before, void* hip_event_after)
   if (kernel != SMOE_KERNEL_NONE && (!hip_event_before || !hip_event_after))
     return fail(SMOE_E_ARG, "null event");
   std::lock_guard<std::mutex> lk(g_trace_mu);
+  const int pending = g_trace_kernel != SMOE_KERNEL_NONE ? 1 : 0;
   g_trace_kernel = kernel;
   g_trace_before = (hipEvent_t)hip_event_before;
   g_trace_after = (hipEvent_t)hip_event_after;
-  return ok();
+  return kernel == SMOE_KERNEL_NONE ? pending : SMOE_OK;
 }
 
 }  // extern "C"

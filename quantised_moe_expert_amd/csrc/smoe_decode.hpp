@@ -84,7 +84,7 @@ __device__ __forceinline__ float block_sum(float v, float* s_tmp) {
 // --------------------------------------------------------------------- K1 --
 
 template <int BITS, typename ST, int VG, bool XF32>
-__global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_gate_up(DecodeArgs A) {
+__global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(DecodeArgs A) {
   constexpr int PPW = QT<BITS>::PPW;
   constexpr int WPW = QT<BITS>::WPW;
   constexpr int NPOS = QT<BITS>::NPOS;
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_gate_up(DecodeArgs A) {
 // --------------------------------------------------------------------- K2 --
 
 template <int BITS, typename ST, int VD>
-__global__ __launch_bounds__(DEC_THREADS, 1) void k_dec_down(DecodeArgs A) {
+__global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(DecodeArgs A) {
   constexpr int PPW = QT<BITS>::PPW;
   constexpr int WPW = QT<BITS>::WPW;
   constexpr int NPOS = QT<BITS>::NPOS;

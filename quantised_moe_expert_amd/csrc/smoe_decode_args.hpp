@@ -10,7 +10,10 @@
 namespace smoe {
 
 constexpr int DEC_THREADS = 512;   // one workgroup of 8 waves per CU
-constexpr int DEC_NWG = 256;       // workgroups per launch
+constexpr int DEC_NWG = 256;       // workgroups per launch (one per CU)
+// waves per SIMD the kernels are built for (HIP's second launch-bounds
+// argument): one 8-wave workgroup per CU
+constexpr int DEC_WAVES_PER_EU = DEC_THREADS / 256;
 constexpr int DEC_RB_MAX = 64;     // down-projection rows per workgroup, max
 constexpr int DEC_XW = 4;          // x code words per thread (d * bits / 32 <= 4 * 512)
 constexpr int DEC_HJ = 2;          // h vectors staged per wave (k <= 16)

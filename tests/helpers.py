@@ -127,7 +127,7 @@ class DeviceLayer:
         ids = torch.full((max(T, 1), k), -1, dtype=torch.int32, device=device)
         w = torch.full((max(T, 1), k), float("nan"), dtype=torch.float32, device=device)
         nws = smoe.smoe_workspace_bytes(self.handle, T, k)
-        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nws, 256), dtype=torch.uint8, device=device)
         smoe.smoe_moe_forward(self.handle, xt.data_ptr(),
                               smoe.SMOE_DTYPE_BF16 if x_dtype == "bf16" else smoe.SMOE_DTYPE_F32,
                               lg.data_ptr(), T, k, norm, out.data_ptr(), ids.data_ptr(),

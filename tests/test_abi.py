@@ -192,4 +192,5 @@ def test_trace_kernel_argument_checks():
     with pytest.raises(smoe.SmoeError):
         smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_GATE_UP, 0, FAKE)
     smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_DOWN, FAKE, FAKE)
-    smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_NONE)  # disarm
+    assert smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_NONE) == 1  # was armed, never fired
+    assert smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_NONE) == 0

@@ -186,6 +186,32 @@ def test_single_token_repeated_launches_and_streams():
     assert rel_l2(out, ref[1]) <= TOL
 
 
+def test_single_token_workspace_reuse():
+    # many one-token forwards on one workspace, two layers, alternating
+    torch = _torch()
+    import quantised_moe_expert_amd as smoe
+    hl = random_layer(31, 4096, 1536, 16, 4)
+    hl2 = random_layer(32, 4096, 1536, 16, 4)
+    dl, dl2 = DeviceLayer(hl), DeviceLayer(hl2)
+    r = synth.rng(33)
+    x = _x(r, 1, 4096, "bf16")
+    lgs = [synth.normal_f32(r, (1, 16)) for _ in range(4)]
+    refs = [O.moe_forward(hl.oracle(), x, lg, 8, True)[0] for lg in lgs]
+    refs2 = [O.moe_forward(hl2.oracle(), x, lg, 8, True)[0] for lg in lgs]
+    nws = smoe.smoe_workspace_bytes(dl.handle, 1, 8)
+    ws = torch.zeros(nws, dtype=torch.uint8, device="cuda")
+    xt = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda().to(torch.bfloat16)
+    out = torch.empty((1, 4096), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for i in range(24):
+        lg = torch.from_numpy(lgs[i % 4]).cuda()
+        layer, ref = (dl, refs) if i % 2 == 0 else (dl2, refs2)
+        smoe.smoe_moe_forward(layer.handle, xt.data_ptr(), smoe.SMOE_DTYPE_BF16, lg.data_ptr(), 1,
+                              8, True, out.data_ptr(), 0, 0, ws.data_ptr(), nws, s)
+        torch.cuda.synchronize()
+        assert rel_l2(out.cpu().numpy(), ref[i % 4]) <= TOL, i
+
+
 def test_decode_step_multi_token_small():
     torch = _torch()
     import quantised_moe_expert_amd as smoe
@@ -198,7 +224,7 @@ def test_decode_step_multi_token_small():
     h_d = torch.from_numpy(x.copy()).cuda()
     lg_d = torch.from_numpy(lg).cuda()
     nws = smoe.smoe_workspace_bytes(dls[0].handle, T, 4)
-    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nws, dtype=torch.uint8, device="cuda")
     smoe.smoe_decode_step([d.handle for d in dls], h_d.data_ptr(), lg_d.data_ptr(), T, 4, False,
                           1e-6, ws.data_ptr(), nws, 0)
     torch.cuda.synchronize()
@@ -281,7 +307,7 @@ def test_qwen_stack_three_layers_full_width():
     h_d = torch.from_numpy(x.copy()).cuda()
     lg_d = torch.from_numpy(lg).cuda()
     nws = smoe.smoe_workspace_bytes(dls[0].handle, 1, W.top_k)
-    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nws, dtype=torch.uint8, device="cuda")
     smoe.smoe_decode_step([d.handle for d in dls], h_d.data_ptr(), lg_d.data_ptr(), 1, W.top_k,
                           True, 1e-6, ws.data_ptr(), nws, 0)
     torch.cuda.synchronize()
