@@ -12,6 +12,32 @@ namespace smoe {
 #define SMOE_V_LIST(X) \
   X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
 
+// Grouped stages: 4-wave workgroups (see smoe_gemv.hpp).
+constexpr int GV_THREADS = 256;
+constexpr int GV_WAVES = GV_THREADS / 64;
+
+// Activation forms of the staged vectors.
+enum GvIn { GV_BF16 = 0, GV_F32_SPLIT = 1, GV_F32 = 2 };
+
+// LDS layout of one chunk (in 32-bit words): hi pairs [TC][cols/2], lo pairs
+// [TC][cols/2] (split only), K [TC][NK * LPR], output scale [TC], and the
+// per-wave statistics [TC][GV_WAVES][2].
+struct GvLds {
+  int xhi, xlo, k, osc, red, total;
+};
+
+__host__ __device__ inline GvLds gv_lds_layout(int cols, int lpr, int nk, int tc, bool split) {
+  GvLds L;
+  const int xs = cols / 2;
+  L.xhi = 0;
+  L.xlo = tc * xs;
+  L.k = L.xlo + (split ? tc * xs : 0);
+  L.osc = L.k + tc * nk * lpr;
+  L.red = L.osc + tc;
+  L.total = L.red + tc * GV_WAVES * 2;
+  return L;
+}
+
 struct MatArgs {
   uint64_t codes_off, scales_off;
   int rows, cols, words_per_row, lpr_log2;
@@ -23,7 +49,8 @@ struct GemvArgs {
   int shared;            // 1: one expert (the shared one), all tokens, pair = token
   int T;
   MatArgs m0, m1;        // gate/up (m1 used by the gate/up stage only)
-  int rows_per_wave;
+  int rows_per_wave;     // a multiple of the rows one wave covers per step
+  int tc;                // tokens staged in LDS per chunk
   const void* x;         // activations: gate/up: [T, cols]; down: h [pairs, cols]
   int x_ld;              // elements between consecutive activation vectors
   int rms;               // gate/up: apply unit-gain RMSNorm to x
@@ -38,8 +65,8 @@ struct GemvArgs {
 // Launchers, defined in smoe_gemv.hpp and instantiated per (BITS, scale
 // type, V) by the smoe_gemv_inst.hip units.
 template <int BITS, typename ST, int V>
-hipError_t launch_gu(const GemvArgs& A, bool bf16, dim3 grid, hipStream_t s);
+hipError_t launch_gu(const GemvArgs& A, int in, dim3 grid, unsigned lds, hipStream_t s);
 template <int BITS, typename ST, int V>
-hipError_t launch_dn(const GemvArgs& A, dim3 grid, hipStream_t s);
+hipError_t launch_dn(const GemvArgs& A, dim3 grid, unsigned lds, hipStream_t s);
 
 }  // namespace smoe

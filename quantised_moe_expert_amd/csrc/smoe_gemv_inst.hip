@@ -12,10 +12,11 @@
 namespace smoe {
 
 #define SMOE_INST(n)                                                                      \
-  template hipError_t launch_gu<SMOE_INST_BITS, SMOE_INST_ST, n>(const GemvArgs&, bool,   \
-                                                                 dim3, hipStream_t);      \
+  template hipError_t launch_gu<SMOE_INST_BITS, SMOE_INST_ST, n>(const GemvArgs&, int,    \
+                                                                 dim3, unsigned,          \
+                                                                 hipStream_t);            \
   template hipError_t launch_dn<SMOE_INST_BITS, SMOE_INST_ST, n>(const GemvArgs&, dim3,   \
-                                                                 hipStream_t);
+                                                                 unsigned, hipStream_t);
 
 #if SMOE_INST_VLO <= 1 && 1 <= SMOE_INST_VHI
 SMOE_INST(1)

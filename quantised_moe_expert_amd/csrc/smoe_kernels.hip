@@ -236,25 +236,42 @@ static MatArgs mat_args(const MatPlan& m) {
 }
 
 template <int BITS, typename ST>
-static hipError_t gate_up_dispatch(int v, bool bf16, dim3 grid, hipStream_t s, const GemvArgs& A) {
+static hipError_t gate_up_dispatch(int v, int in, dim3 grid, unsigned lds, hipStream_t s,
+                                   const GemvArgs& A) {
 #define SMOE_GU_CASE(n) \
-  if (v == n) return launch_gu<BITS, ST, n>(A, bf16, grid, s);
+  if (v == n) return launch_gu<BITS, ST, n>(A, in, grid, lds, s);
   SMOE_V_LIST(SMOE_GU_CASE)
 #undef SMOE_GU_CASE
   return hipErrorInvalidValue;
 }
 
 template <int BITS, typename ST>
-static hipError_t down_dispatch(int v, dim3 grid, hipStream_t s, const GemvArgs& A) {
+static hipError_t down_dispatch(int v, dim3 grid, unsigned lds, hipStream_t s, const GemvArgs& A) {
 #define SMOE_DN_CASE(n) \
-  if (v == n) return launch_dn<BITS, ST, n>(A, grid, s);
+  if (v == n) return launch_dn<BITS, ST, n>(A, grid, lds, s);
   SMOE_V_LIST(SMOE_DN_CASE)
 #undef SMOE_DN_CASE
   return hipErrorInvalidValue;
 }
 
-static int rows_per_wave_for(const MatPlan& m, int mult) {
-  return (64 >> m.lpr_log2) * mult;
+// Launch shape of a grouped stage over `slots` expert slots: rows per wave
+// (whole row groups, up to 8, fewer when that leaves under ~2048 workgroups)
+// and tokens staged per chunk (as many as fit in 48 KB of LDS, at most 8).
+static void grouped_shape(const MatPlan& m, bool split, int slots, GemvArgs& A, dim3& grid,
+                          unsigned& lds) {
+  const int RPW = 64 >> m.lpr_log2, LPR = 1 << m.lpr_log2;
+  const int groups = (m.rows + RPW - 1) / RPW;
+  int gpw = (int)((int64_t)groups * slots / (GV_WAVES * 2048));
+  gpw = gpw < 1 ? 1 : (gpw > 8 ? 8 : gpw);
+  A.rows_per_wave = gpw * RPW;
+  const int rpb = A.rows_per_wave * GV_WAVES;
+  grid = dim3((m.rows + rpb - 1) / rpb, slots);
+  const int nk = m.v / 4 + m.v % 4;
+  const int per_token = (m.cols / 2 * (split ? 2 : 1) + nk * LPR + 1 + GV_WAVES * 2) * 4;
+  int tc = 49152 / per_token;
+  tc = tc < 1 ? 1 : (tc > 8 ? 8 : tc);
+  A.tc = tc;
+  lds = (unsigned)gv_lds_layout(m.cols, LPR, nk, tc, split).total * 4;
 }
 
 hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xmode,
@@ -269,7 +286,6 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
   A.T = T;
   A.m0 = mat_args(P.gate);
   A.m1 = mat_args(P.up);
-  A.rows_per_wave = rows_per_wave_for(P.gate, 4);
   A.x = x;
   A.x_ld = P.d_model;
   A.rms = xmode == X_F32_RMS;
@@ -279,16 +295,18 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
   A.offs = offs;
   A.pair_token = pair_token;
   A.out = h;
-  const int rows_per_block = A.rows_per_wave * 4;
-  dim3 grid((P.gate.rows + rows_per_block - 1) / rows_per_block, shared ? 1 : max_slots);
+  const int in = xmode == X_BF16 ? GV_BF16 : GV_F32_SPLIT;
+  dim3 grid;
+  unsigned lds;
+  grouped_shape(P.gate, in == GV_F32_SPLIT, shared ? 1 : max_slots, A, grid, lds);
   const int v = P.gate.v;
   if (L.desc.bits == 4)
     return L.desc.scale_dtype == SMOE_SCALE_F32
-               ? gate_up_dispatch<4, float>(v, xmode == X_BF16, grid, stream, A)
-               : gate_up_dispatch<4, _Float16>(v, xmode == X_BF16, grid, stream, A);
+               ? gate_up_dispatch<4, float>(v, in, grid, lds, stream, A)
+               : gate_up_dispatch<4, _Float16>(v, in, grid, lds, stream, A);
   return L.desc.scale_dtype == SMOE_SCALE_F32
-             ? gate_up_dispatch<2, float>(v, xmode == X_BF16, grid, stream, A)
-             : gate_up_dispatch<2, _Float16>(v, xmode == X_BF16, grid, stream, A);
+             ? gate_up_dispatch<2, float>(v, in, grid, lds, stream, A)
+             : gate_up_dispatch<2, _Float16>(v, in, grid, lds, stream, A);
 }
 
 hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int max_slots,
@@ -302,21 +320,22 @@ hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, i
   A.T = T;
   A.m0 = mat_args(P.down);
   A.m1 = A.m0;
-  A.rows_per_wave = rows_per_wave_for(P.down, 16);
   A.x = h;
   A.x_ld = P.ffn;
   A.meta = meta;
   A.active = active;
   A.offs = offs;
   A.out = y;
-  const int rows_per_block = A.rows_per_wave * 4;
-  dim3 grid((P.down.rows + rows_per_block - 1) / rows_per_block, shared ? 1 : max_slots);
+  dim3 grid;
+  unsigned lds;
+  grouped_shape(P.down, false, shared ? 1 : max_slots, A, grid, lds);
   const int v = P.down.v;
   if (L.desc.bits == 4)
-    return L.desc.scale_dtype == SMOE_SCALE_F32 ? down_dispatch<4, float>(v, grid, stream, A)
-                                                : down_dispatch<4, _Float16>(v, grid, stream, A);
-  return L.desc.scale_dtype == SMOE_SCALE_F32 ? down_dispatch<2, float>(v, grid, stream, A)
-                                              : down_dispatch<2, _Float16>(v, grid, stream, A);
+    return L.desc.scale_dtype == SMOE_SCALE_F32
+               ? down_dispatch<4, float>(v, grid, lds, stream, A)
+               : down_dispatch<4, _Float16>(v, grid, lds, stream, A);
+  return L.desc.scale_dtype == SMOE_SCALE_F32 ? down_dispatch<2, float>(v, grid, lds, stream, A)
+                                              : down_dispatch<2, _Float16>(v, grid, lds, stream, A);
 }
 
 }  // namespace smoe

@@ -26,6 +26,17 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t s, Args...
   return hipGetLastError();
 }
 
+template <typename... Args, typename K>
+hipError_t launch_kernel_lds(K kernel, dim3 grid, dim3 block, unsigned lds, hipStream_t s,
+                             Args... args) {
+  if (t_launch_events.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, t_launch_events.start,
+                          t_launch_events.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  return hipGetLastError();
+}
+
 // Takes the armed events when the hook is armed for `kernel` (disarming it)
 // and attaches them to the launches made in this scope.
 bool trace_take(int kernel, hipEvent_t* start, hipEvent_t* stop);
