@@ -165,7 +165,7 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
     return rc;
   {
     TracedLaunch t(SMOE_KERNEL_GATE_UP);
-    rc = check_hip(launch_gate_up(L, false, x, xmode, eps, T, max_slots, meta, active, offs,
+    rc = check_hip(launch_gate_up(L, false, x, xmode, eps, T, T * k, max_slots, meta, active, offs,
                                   pair_token, h, s),
                    "gate/up launch");
   }
@@ -174,17 +174,17 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
   if (L.desc.shared_ffn_dim) {
     float* hsh = (float*)(ws + W.h_shared);
     ysh = (float*)(ws + W.y_shared);
-    if ((rc = check_hip(launch_gate_up(L, true, x, xmode, eps, T, 1, meta, active, offs,
+    if ((rc = check_hip(launch_gate_up(L, true, x, xmode, eps, T, T, 1, meta, active, offs,
                                        pair_token, hsh, s),
                         "shared gate/up launch")))
       return rc;
-    if ((rc = check_hip(launch_down(L, true, hsh, T, 1, meta, active, offs, ysh, s),
+    if ((rc = check_hip(launch_down(L, true, hsh, T, T, 1, meta, active, offs, ysh, s),
                         "shared down launch")))
       return rc;
   }
   {
     TracedLaunch t(SMOE_KERNEL_DOWN);
-    rc = check_hip(launch_down(L, false, h, T, max_slots, meta, active, offs, y, s),
+    rc = check_hip(launch_down(L, false, h, T, T * k, max_slots, meta, active, offs, y, s),
                    "down launch");
   }
   if (rc) return rc;

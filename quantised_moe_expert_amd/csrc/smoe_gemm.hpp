@@ -1,0 +1,458 @@
+// Grouped expert stages for batches on the matrix cores (gate/up + SwiGLU,
+// and down), v_mfma_f32_16x16x32_f16.
+//
+// Grid (row blocks, active-expert slots), 4-wave workgroups. Per MFMA the M
+// dimension is up to 16 tokens of the slot, N is 16 weight rows, K is 32
+// weights of one scale group; a group (64 weights) takes two MFMAs.
+//   - B (weights): lane l holds row l % 16, k-block b = l / 16 of each
+//     MFMA: for Q4 one word per MFMA, for Q2 one word whose low pairs feed
+//     the first MFMA and high pairs the second. Lanes load 16 bytes of their
+//     row (two Q4 groups or four Q2 groups per wave-wide load) and cross-
+//     lane swaps hand each quarter its k-blocks. A word becomes fp16 pairs
+//     1024 + code * 2^p by one v_and_or_b32 per pair.
+//   - A (tokens): the slot's token vectors staged once per workgroup in LDS
+//     as fp16 pairs pre-divided by 2^p (scaled per token by a power of two so
+//     the largest magnitude sits just below 2^14), in the same pair order as
+//     the decoded words, laid out so that the 16 token rows of one word are
+//     contiguous; lanes of token rows past the chunk read stale rows whose
+//     D rows are dropped.
+//   - per group, with D the two MFMAs' sum: acc += scale[row][g] *
+//     (D - K[g][token]), where K = sum over the group of the staged pairs
+//     times (1024 + m * 2^p) removes both the 1024 offsets and the code
+//     midpoint m.
+// When the grid would have few workgroups (the shared expert), the four
+// waves split the groups of one 16-row tile and add their partial sums in
+// LDS.
+
+#pragma once
+
+#include <type_traits>
+
+#include "smoe_device.hpp"
+#include "smoe_gemv.hpp"
+#include "smoe_gemv_args.hpp"
+#include "smoe_launch.hpp"
+
+#ifndef SMOE_GM_GB
+#define SMOE_GM_GB (GU ? 4 : 8)
+#endif
+
+
+namespace smoe {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f32x4m __attribute__((ext_vector_type(4)));
+
+// Stage pairs [pc, pc + nt) of the slot for the matrix-core stage.
+template <int BITS, int IN, bool GU>
+__device__ __forceinline__ void gm_stage(const GemvArgs& A, const MatArgs& M, uint32_t* lds,
+                                         const GmLds& L, int pc, int nt) {
+  constexpr int WPW = QT<BITS>::WPW, PPW = QT<BITS>::PPW, NPOS = QT<BITS>::NPOS;
+  constexpr int WPG = QT<BITS>::WPG;  // words per group
+  constexpr bool XF32 = IN != GV_BF16, SPLIT = IN == GV_F32_SPLIT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cols = M.cols, Wr = M.words_per_row, G = cols / 64, TC = A.tc;
+  const size_t esz = XF32 ? 4 : 2;
+  auto vec = [&](int i) {
+    const int p = pc + i;
+    const int t = (GU && !A.shared) ? A.pair_token[p] : p;
+    return (const void*)((const uint8_t*)A.x + (size_t)t * A.x_ld * esz);
+  };
+  float* red = (float*)(lds + L.red);
+  for (int i = 0; i < nt; ++i) {
+    const void* v = vec(i);
+    float amax = 0.f, ss = 0.f;
+    for (int cw = tid; cw < Wr; cw += GV_THREADS) {
+      float xv[WPW];
+      gv_load_word<BITS, XF32>(v, cw, xv);
+#pragma unroll
+      for (int j = 0; j < WPW; ++j) {
+        amax = fmaxf(amax, fabsf(xv[j]));
+        ss = fmaf(xv[j], xv[j], ss);
+      }
+    }
+    amax = lane63(seg_max(amax, 6));
+    ss = lane63(seg_sum(ss, 6));
+    if (lane == 0) {
+      red[(i * GV_WAVES + wave) * 2] = amax;
+      red[(i * GV_WAVES + wave) * 2 + 1] = ss;
+    }
+  }
+  __syncthreads();
+  float* Kl = (float*)(lds + L.k);
+  float* osc = (float*)(lds + L.osc);
+  uint32_t* X = lds + L.x;
+  uint32_t* Xlo = lds + L.xlo;
+  // unit (g, i): group g of token i; pairs of word cw for token i go to
+  // X[((cw * HALVES + hv) * TC + i) * 4 + (q % 4)] with hv = q / 4 (split
+  // inputs: the hi halves there, the lo halves at the same place in Xlo)
+  constexpr int HALVES = PPW / 4;
+  for (int u = tid; u < G * nt; u += GV_THREADS) {
+    const int i = u / G, g = u - i * G;
+    float m = 0.f, q2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < GV_WAVES; ++w) {
+      m = fmaxf(m, red[(i * GV_WAVES + w) * 2]);
+      q2 += red[(i * GV_WAVES + w) * 2 + 1];
+    }
+    int ex = 0;
+    frexpf(m, &ex);
+    ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+    const float S = ldexpf(1.0f, 14 - ex);
+    if (g == 0) {
+      const float r = A.rms ? 1.0f / sqrtf(q2 / (float)cols + A.eps) : 1.0f;
+      osc[i] = r / (QT<BITS>::M * S);
+    }
+    const void* v = vec(i);
+    float kk = 0.f;
+#pragma unroll 2
+    for (int j = 0; j < WPG; ++j) {
+      const int cw = g * WPG + j;
+      float xv[WPW];
+      gv_load_word<BITS, XF32>(v, cw, xv);
+#pragma unroll
+      for (int q = 0; q < PPW; ++q) {
+        const int hs = q / NPOS, pos = q % NPOS;
+        const int ia = hs * NPOS + pos, ib = ia + WPW / 2;
+        const float f = S * (1.0f / (float)(1 << (BITS * pos)));
+        const float a = xv[ia] * f, bb = xv[ib] * f;
+        const _Float16 ha = (_Float16)a, hb = (_Float16)bb;
+        const int xi = ((cw * HALVES + q / 4) * TC + i) * 4 + (q % 4);
+        X[xi] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
+        float sumx = (float)ha + (float)hb;
+        if constexpr (SPLIT) {
+          const _Float16 la = (_Float16)(a - (float)ha), lb = (_Float16)(bb - (float)hb);
+          Xlo[xi] = __builtin_bit_cast(uint32_t, f16x2{la, lb});
+          sumx += (float)la + (float)lb;
+        }
+        kk = fmaf(sumx, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)), kk);
+      }
+    }
+    Kl[g * 16 + i] = kk;
+  }
+  // K of the token rows past the chunk (their D rows are never used)
+  for (int u = tid; u < G * 16; u += GV_THREADS)
+    if ((u & 15) >= nt) Kl[u] = 0.f;
+  __syncthreads();
+}
+
+// A constant in a scalar register the optimiser cannot see through.
+__device__ __forceinline__ uint32_t gm_sreg(uint32_t c) {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(c));
+  return r;
+}
+
+// Decoded fp16 pairs 4h .. 4h + 3 of a code word, as one MFMA operand.
+// (v & mask) | magic is written in C with the mask in an SGPR and the magic
+// in a VGPR, so the compiler emits one v_and_or_b32 of its own: an MFMA that
+// reads a VGPR written by VALU code needs wait states, and the compiler
+// counts them only for instructions it generated (not for inline asm).
+template <int BITS>
+__device__ __forceinline__ h8 gm_operand(uint32_t w, int h, uint32_t magic) {
+  constexpr int NPOS = QT<BITS>::NPOS;
+  constexpr uint32_t base = (1u << BITS) - 1u;
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = 4 * h + j, hs = q / NPOS, pos = q % NPOS;
+    const uint32_t v = hs ? (w >> 8) : w;
+    const uint32_t m = gm_sreg((base << (BITS * pos)) | (base << (BITS * pos + 16)));
+    p[j] = (v & m) | magic;
+  }
+  const u32x4 t = {p[0], p[1], p[2], p[3]};
+  return __builtin_bit_cast(h8, t);
+}
+
+// Scales of groups g0 .. g0 + 3 of one row. SV: the row holds a multiple of
+// four groups and g0 is a multiple of four (one vector load; a quad past the
+// row is read from the row's last quad); else one load per group, clamped to
+// the row. The caller zeroes the scales of groups it does not own.
+template <typename ST, bool SV>
+__device__ __forceinline__ void gm_scales4(const ST* rs, int g0, int G, float* out) {
+  if constexpr (SV) {
+    const int q = min(g0, G - 4);
+    if constexpr (sizeof(ST) == 4) {
+      const u32x4 t = *(const u32x4_a4*)(rs + q);
+      // components go through named scalars: a bit_cast of a vector
+      // component expression reads component 0
+      const uint32_t t0 = t.x, t1 = t.y, t2 = t.z, t3 = t.w;
+      out[0] = __builtin_bit_cast(float, t0);
+      out[1] = __builtin_bit_cast(float, t1);
+      out[2] = __builtin_bit_cast(float, t2);
+      out[3] = __builtin_bit_cast(float, t3);
+    } else {
+      const u32x2 t = *(const u32x2_a4*)(rs + q);
+      const uint32_t lo = t.x, hi = t.y;
+      const f16x2 a = __builtin_bit_cast(f16x2, lo), c = __builtin_bit_cast(f16x2, hi);
+      const _Float16 a0 = a.x, a1 = a.y, c0 = c.x, c1 = c.y;
+      out[0] = (float)a0;
+      out[1] = (float)a1;
+      out[2] = (float)c0;
+      out[3] = (float)c1;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = load_scale<ST, false>(rs + min(g0 + j, G - 1));
+  }
+}
+
+// v_permlane32_swap: lanes 32..63 of a trade places with lanes 0..31 of c.
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& c) {
+  const auto t = __builtin_amdgcn_permlane32_swap(a, c, false, false);
+  a = t[0];
+  c = t[1];
+}
+// v_permlane16_swap: lanes 16..31 and 48..63 of a trade places with lanes
+// 0..15 and 32..47 of c.
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& c) {
+  const auto t = __builtin_amdgcn_permlane16_swap(a, c, false, false);
+  a = t[0];
+  c = t[1];
+}
+
+// Code words of one load unit of a row: 16 bytes per lane, 2 groups for Q4
+// and 4 for Q2. Lane quarter b = lane / 16 loads
+//   Q4: words (b & 1) * 4 .. + 3 of group u0 + (b >> 1);
+//   Q2: all four words of group u0 + b
+// (groups past the row read its last group; their results are unused). A
+// lane reads 16 bytes, twice the words of one k-block, so that each load
+// instruction moves a full kilobyte.
+template <int BITS>
+__device__ __forceinline__ u32x4 gm_unit_load(const uint32_t* row_codes, int u0, int G, int b) {
+  constexpr int WPG = QT<BITS>::WPG;
+  const int g = min(u0 + (BITS == 4 ? (b >> 1) : b), G - 1);
+  return *(const u32x4*)(row_codes + g * WPG + (BITS == 4 ? (b & 1) * 4 : 0));
+}
+
+// Swaps across lane quarters that give every quarter one k-block of each
+// group of a loaded unit:
+//   Q4: w[0], w[1] hold words wmap(b), wmap(b) + 1 of the unit's first
+//       group (one per MFMA) and w[2], w[3] the same words of the second,
+//       with wmap(b) = (b & 1) * 4 + (b >> 1) * 2;
+//   Q2: a 4 x 4 transpose: w[j] holds word b of the unit's group j.
+template <int BITS>
+__device__ __forceinline__ void gm_unit_arrange(const u32x4& t, uint32_t w[4]) {
+  w[0] = t.x;
+  w[1] = t.y;
+  w[2] = t.z;
+  w[3] = t.w;
+  swap32(w[0], w[2]);
+  swap32(w[1], w[3]);
+  if constexpr (BITS == 2) {
+    swap16(w[0], w[1]);
+    swap16(w[2], w[3]);
+  }
+}
+
+template <int BITS, typename ST, int IN, bool GU, bool SV>
+__global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
+  extern __shared__ uint32_t lds[];
+  constexpr int WPG = QT<BITS>::WPG, HALVES = QT<BITS>::PPW / 4;
+  constexpr int GB = SMOE_GM_GB;  // groups per load batch (multiple of 4)
+  static_assert(GB % 4 == 0, "batches start at multiples of four groups");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int e = 0, p0, p1;
+  if (A.shared) {
+    p0 = 0;
+    p1 = A.T;
+  } else {
+    const int slot = blockIdx.y;
+    if (slot >= A.meta[0]) return;  // workgroup-uniform
+    e = A.active[slot];
+    p0 = A.offs[slot];
+    p1 = A.offs[slot + 1];
+  }
+  if (p0 >= p1) return;  // workgroup-uniform
+  const MatArgs& M0 = A.m0;
+  const int rows = M0.rows, Wr = M0.words_per_row, G = M0.cols / 64, TC = A.tc;
+  const int ks = A.ksplit;  // waves per 16-row tile: 1 or 4
+  const int tile = wave / ks, kpart = wave - tile * ks;
+  const int row0 = (blockIdx.x * (GV_WAVES / ks) + tile) * 16;
+  const int r = lane & 15, b = lane >> 4;
+  const int row = row0 + r, rc = row < rows ? row : rows - 1;
+  const int gper = ((G + ks - 1) / ks + 3) & ~3;  // a multiple of four groups
+  const int gb0 = min(G, kpart * gper), gb1 = min(G, gb0 + gper);
+  const uint8_t* blob = A.blobs + (uint64_t)e * A.stride;
+  const uint32_t* c0 = (const uint32_t*)(blob + M0.codes_off) + (size_t)rc * Wr;
+  const ST* s0 = (const ST*)(blob + M0.scales_off) + (size_t)rc * G;
+  const uint32_t* c1 = (const uint32_t*)(blob + A.m1.codes_off) + (size_t)rc * Wr;
+  const ST* s1 = (const ST*)(blob + A.m1.scales_off) + (size_t)rc * G;
+  constexpr bool SPLIT = IN == GV_F32_SPLIT;
+  const GmLds L = gm_lds_layout(M0.cols, TC, SPLIT);
+  const uint32_t* X = lds + L.x;
+  const uint32_t* Xlo = lds + L.xlo;
+  const float* Kl = (const float*)(lds + L.k);
+  const float* osc = (const float*)(lds + L.osc);
+  float* part = (float*)(lds + L.part);
+  // the fp16 pair 1024, 1024 in a VGPR (an operand of the decode)
+  uint32_t magic;
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  // first word of a group this lane feeds to the MFMAs (after the swaps)
+  const int wmap = BITS == 4 ? (b & 1) * 4 + (b >> 1) * 2 : b;
+  constexpr int UG = BITS == 4 ? 2 : 4;  // groups per load unit
+  constexpr int NU = GB / UG;             // load units per batch
+  struct Batch {
+    u32x4 wa[NU], wb[NU];
+    float sa[GB], sb[GB];
+  };
+  auto load = [&](Batch& B, int g0) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      B.wa[u] = gm_unit_load<BITS>(c0, g0 + u * UG, G, b);
+      if constexpr (GU) B.wb[u] = gm_unit_load<BITS>(c1, g0 + u * UG, G, b);
+    }
+#pragma unroll
+    for (int q = 0; q < GB / 4; ++q) {
+      gm_scales4<ST, SV>(s0, g0 + 4 * q, G, B.sa + 4 * q);
+      if constexpr (GU) gm_scales4<ST, SV>(s1, g0 + 4 * q, G, B.sb + 4 * q);
+    }
+  };
+  // the word that group j of an arranged batch feeds to MFMA h
+  auto word = [&](const uint32_t (*w)[4], int j, int h) -> uint32_t {
+    if constexpr (BITS == 4) return w[j / 2][(j % 2) * 2 + h];
+    return w[j / 4][j % 4];
+  };
+
+  Batch bA, bB;
+  load(bA, gb0);  // in flight while the tokens are staged
+  for (int pc = p0; pc < p1; pc += TC) {
+    const int nt = min(TC, p1 - pc);
+    if (pc > p0) {
+      __syncthreads();  // the previous chunk's readers are done
+      load(bA, gb0);
+    }
+    gm_stage<BITS, IN, GU>(A, M0, lds, L, pc, nt);
+    // A row r of the MFMAs is token r; rows past the chunk read whatever the
+    // LDS holds (row TC - 1 past the staged block) and their D rows are
+    // never used
+    const int rr = min(r, TC - 1);
+    f32x4m acc_a = {0.f, 0.f, 0.f, 0.f}, acc_b = {0.f, 0.f, 0.f, 0.f};
+    // groups g0 .. g0 + GB - 1; those at or past gb1 (the tail of the
+    // wave's range) count with scale zero and read the last group's LDS
+    auto compute = [&](const Batch& B, int g0) {
+      uint32_t wa[NU][4], wb[NU][4];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        gm_unit_arrange<BITS>(B.wa[u], wa[u]);
+        if constexpr (GU) gm_unit_arrange<BITS>(B.wb[u], wb[u]);
+      }
+#pragma unroll
+      for (int j = 0; j < GB; ++j) {
+        const bool own = g0 + j < gb1;  // wave-uniform
+        const int g = min(g0 + j, G - 1);
+        const float sa = own ? B.sa[j] : 0.f;
+        f32x4m da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int hv = BITS == 4 ? 0 : h;
+          const int cw = BITS == 4 ? g * WPG + wmap + h : g * WPG + wmap;
+          const int xi = ((cw * HALVES + hv) * TC + rr) * 4;
+          const h8 av = __builtin_bit_cast(h8, *(const u32x4*)(X + xi));
+          const h8 oa = gm_operand<BITS>(word(wa, j, BITS == 4 ? h : 0), hv, magic);
+          da = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, oa, da, 0, 0, 0);
+          h8 ob;
+          if constexpr (GU) {
+            ob = gm_operand<BITS>(word(wb, j, BITS == 4 ? h : 0), hv, magic);
+            db = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ob, db, 0, 0, 0);
+          }
+          if constexpr (SPLIT) {
+            const h8 al = __builtin_bit_cast(h8, *(const u32x4*)(Xlo + xi));
+            da = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, oa, da, 0, 0, 0);
+            if constexpr (GU) db = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, ob, db, 0, 0, 0);
+          }
+        }
+        const f32x4m kv = *(const f32x4m*)(Kl + g * 16 + 4 * b);
+        const float a0 = da.x, a1 = da.y, a2 = da.z, a3 = da.w;
+        const float k0 = kv.x, k1 = kv.y, k2 = kv.z, k3 = kv.w;
+        acc_a.x = fmaf(sa, a0 - k0, acc_a.x);
+        acc_a.y = fmaf(sa, a1 - k1, acc_a.y);
+        acc_a.z = fmaf(sa, a2 - k2, acc_a.z);
+        acc_a.w = fmaf(sa, a3 - k3, acc_a.w);
+        if constexpr (GU) {
+          const float sb = own ? B.sb[j] : 0.f;
+          const float b0 = db.x, b1 = db.y, b2 = db.z, b3 = db.w;
+          acc_b.x = fmaf(sb, b0 - k0, acc_b.x);
+          acc_b.y = fmaf(sb, b1 - k1, acc_b.y);
+          acc_b.z = fmaf(sb, b2 - k2, acc_b.z);
+          acc_b.w = fmaf(sb, b3 - k3, acc_b.w);
+        }
+      }
+    };
+    // Loads are unconditional (past the row they re-read its last group, a
+    // cache hit) so that the number in flight is the same on every path and
+    // each wait covers exactly the batch about to be used.
+    // Scheduling barriers keep each batch's loads ahead of the computation
+    // on the other batch (the scheduler would otherwise sink them past it).
+    for (int g0 = gb0; g0 < gb1; g0 += 2 * GB) {
+      load(bB, g0 + GB);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(bA, g0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(bA, g0 + 2 * GB);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g0 + GB < gb1) compute(bB, g0 + GB);
+    }
+    // partial sums of the k-split waves meet in LDS
+    float va[4] = {acc_a.x, acc_a.y, acc_a.z, acc_a.w};
+    float vb[4] = {acc_b.x, acc_b.y, acc_b.z, acc_b.w};
+    if (ks > 1) {
+      if (kpart > 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          part[((tile * 4 + kpart) * 64 + lane) * 8 + i] = va[i];
+          part[((tile * 4 + kpart) * 64 + lane) * 8 + 4 + i] = vb[i];
+        }
+      }
+      __syncthreads();
+      if (kpart == 0) {
+        for (int kp = 1; kp < ks; ++kp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            va[i] += part[((tile * 4 + kp) * 64 + lane) * 8 + i];
+            vb[i] += part[((tile * 4 + kp) * 64 + lane) * 8 + 4 + i];
+          }
+      }
+    }
+    if (kpart == 0 && row < rows) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * b + i;
+        if (t < nt) {
+          const float o = osc[t];
+          float val;
+          if constexpr (GU) {
+            const float gg = va[i] * o, uu = vb[i] * o;
+            val = gg / (1.0f + expf(-gg)) * uu;
+          } else {
+            val = va[i] * o;
+          }
+          A.out[(size_t)(pc + t) * rows + row] = val;
+        }
+      }
+    }
+  }
+}
+
+// Launcher, instantiated per (BITS, scale type) in smoe_gemm_inst.hip.
+template <int BITS, typename ST, bool SV>
+static hipError_t launch_gm_sv(const GemvArgs& A, bool gate_up, int in, dim3 grid, unsigned lds,
+                               hipStream_t s) {
+  const dim3 block(GV_THREADS);
+  if (!gate_up)
+    return launch_kernel_lds(k_gemm<BITS, ST, GV_F32, false, SV>, grid, block, lds, s, A);
+  if (in == GV_BF16)
+    return launch_kernel_lds(k_gemm<BITS, ST, GV_BF16, true, SV>, grid, block, lds, s, A);
+  return launch_kernel_lds(k_gemm<BITS, ST, GV_F32_SPLIT, true, SV>, grid, block, lds, s, A);
+}
+
+template <int BITS, typename ST>
+hipError_t launch_gm(const GemvArgs& A, bool gate_up, int in, dim3 grid, unsigned lds,
+                     hipStream_t s) {
+  // vector scale loads when every row holds a whole number of scale quads
+  if (A.m0.cols / 64 % 4 == 0) return launch_gm_sv<BITS, ST, true>(A, gate_up, in, grid, lds, s);
+  return launch_gm_sv<BITS, ST, false>(A, gate_up, in, grid, lds, s);
+}
+
+}  // namespace smoe

@@ -38,6 +38,27 @@ __host__ __device__ inline GvLds gv_lds_layout(int cols, int lpr, int nk, int tc
   return L;
 }
 
+// LDS layout of the matrix-core stage (32-bit words): token pairs [TC * cols
+// / 2] (+ the same again for the lo halves of split inputs), K [G][16],
+// output scales [16], per-wave statistics [TC][GV_WAVES][2], and the k-split
+// partial sums [GV_WAVES][64][8]. Every region starts 16-byte aligned.
+struct GmLds {
+  int x, xlo, k, osc, red, part, total;
+};
+
+__host__ __device__ inline GmLds gm_lds_layout(int cols, int tc, bool split) {
+  auto al4 = [](int n) { return (n + 3) & ~3; };
+  GmLds L;
+  L.x = 0;
+  L.xlo = al4(tc * cols / 2);
+  L.k = L.xlo + (split ? al4(tc * cols / 2) : 0);
+  L.osc = L.k + al4(cols / 64 * 16);
+  L.red = L.osc + 16;
+  L.part = L.red + al4(tc * GV_WAVES * 2);
+  L.total = L.part + GV_WAVES * 64 * 8;
+  return L;
+}
+
 struct MatArgs {
   uint64_t codes_off, scales_off;
   int rows, cols, words_per_row, lpr_log2;
@@ -51,6 +72,7 @@ struct GemvArgs {
   MatArgs m0, m1;        // gate/up (m1 used by the gate/up stage only)
   int rows_per_wave;     // a multiple of the rows one wave covers per step
   int tc;                // tokens staged in LDS per chunk
+  int ksplit;            // matrix-core stage: waves sharing one 16-row tile
   const void* x;         // activations: gate/up: [T, cols]; down: h [pairs, cols]
   int x_ld;              // elements between consecutive activation vectors
   int rms;               // gate/up: apply unit-gain RMSNorm to x
@@ -68,5 +90,11 @@ template <int BITS, typename ST, int V>
 hipError_t launch_gu(const GemvArgs& A, int in, dim3 grid, unsigned lds, hipStream_t s);
 template <int BITS, typename ST, int V>
 hipError_t launch_dn(const GemvArgs& A, dim3 grid, unsigned lds, hipStream_t s);
+
+// Matrix-core stage launchers (smoe_gemm.hpp, instantiated per (BITS, scale
+// type) by smoe_gemm_inst.hip); in: GvIn of the activations.
+template <int BITS, typename ST>
+hipError_t launch_gm(const GemvArgs& A, bool gate_up, int in, dim3 grid, unsigned lds,
+                     hipStream_t s);
 
 }  // namespace smoe

@@ -60,12 +60,15 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int3
                         int* active, int* offs, int* pair_token, int* pair_of,
                         hipStream_t stream);
 
+// pairs: routed (token, expert) pairs of the call (T for the shared expert),
+// used to size the launch.
 hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xmode,
-                          float rms_eps, int T, int max_slots, const int* meta,
+                          float rms_eps, int T, int pairs, int max_slots, const int* meta,
                           const int* active, const int* offs, const int* pair_token,
                           float* h, hipStream_t stream);
 
-hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int max_slots,
+hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int pairs,
+                       int max_slots,
                        const int* meta, const int* active, const int* offs, float* y,
                        hipStream_t stream);
 

@@ -274,8 +274,46 @@ static void grouped_shape(const MatPlan& m, bool split, int slots, GemvArgs& A, 
   lds = (unsigned)gv_lds_layout(m.cols, LPR, nk, tc, split).total * 4;
 }
 
+// Launch shape of a matrix-core stage: 16-row tiles, one per wave, or one
+// per workgroup with its groups split over the four waves when one tile per
+// wave leaves under 1024 workgroups. Tokens per chunk: twice the mean pairs
+// per slot (at least 4, at most 16, one MFMA's M) so that the LDS a
+// workgroup holds stays small enough for several workgroups per CU, then cut
+// to fit 64 KB; slots with more pairs take several chunks. The k-split
+// partial-sum region (last in the layout) is allocated only when used.
+// False when not even one token fits.
+#ifndef SMOE_GM_TC_MIN
+#define SMOE_GM_TC_MIN 4
+#endif
+static bool gm_shape(const MatPlan& m, bool split, int pairs, int slots, GemvArgs& A, dim3& grid,
+                     unsigned& lds) {
+  const int tiles = (m.rows + 15) / 16;
+  const int ks = (int64_t)(tiles + GV_WAVES - 1) / GV_WAVES * slots < 1024 ? GV_WAVES : 1;
+  A.ksplit = ks;
+  const int tpb = GV_WAVES / ks;
+  grid = dim3((tiles + tpb - 1) / tpb, slots);
+  const int mean = (pairs + slots - 1) / slots;
+  int tc = 2 * mean < SMOE_GM_TC_MIN ? SMOE_GM_TC_MIN : (2 * mean > 16 ? 16 : 2 * mean);
+  auto bytes = [&](int t) {
+    const GmLds L = gm_lds_layout(m.cols, t, split);
+    return (ks > 1 ? L.total : L.part) * 4;
+  };
+  while (tc > 0 && bytes(tc) > 65536) --tc;
+  if (tc == 0) return false;
+  A.tc = tc;
+  lds = (unsigned)bytes(tc);
+  return true;
+}
+
+template <typename ST>
+static hipError_t gm_dispatch(int bits, const GemvArgs& A, bool gate_up, int in, dim3 grid,
+                              unsigned lds, hipStream_t s) {
+  return bits == 4 ? launch_gm<4, ST>(A, gate_up, in, grid, lds, s)
+                   : launch_gm<2, ST>(A, gate_up, in, grid, lds, s);
+}
+
 hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xmode,
-                          float rms_eps, int T, int max_slots, const int* meta,
+                          float rms_eps, int T, int pairs, int max_slots, const int* meta,
                           const int* active, const int* offs, const int* pair_token,
                           float* h, hipStream_t stream) {
   const ExpertPlan& P = shared ? L.shared_plan : L.plan;
@@ -298,6 +336,11 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
   const int in = xmode == X_BF16 ? GV_BF16 : GV_F32_SPLIT;
   dim3 grid;
   unsigned lds;
+  if (gm_shape(P.gate, in == GV_F32_SPLIT, pairs, shared ? 1 : max_slots, A,
+               grid, lds))
+    return L.desc.scale_dtype == SMOE_SCALE_F32
+               ? gm_dispatch<float>(L.desc.bits, A, true, in, grid, lds, stream)
+               : gm_dispatch<_Float16>(L.desc.bits, A, true, in, grid, lds, stream);
   grouped_shape(P.gate, in == GV_F32_SPLIT, shared ? 1 : max_slots, A, grid, lds);
   const int v = P.gate.v;
   if (L.desc.bits == 4)
@@ -309,7 +352,8 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
              : gate_up_dispatch<2, _Float16>(v, in, grid, lds, stream, A);
 }
 
-hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int max_slots,
+hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int pairs,
+                       int max_slots,
                        const int* meta, const int* active, const int* offs, float* y,
                        hipStream_t stream) {
   const ExpertPlan& P = shared ? L.shared_plan : L.plan;
@@ -328,6 +372,10 @@ hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, i
   A.out = y;
   dim3 grid;
   unsigned lds;
+  if (gm_shape(P.down, false, pairs, shared ? 1 : max_slots, A, grid, lds))
+    return L.desc.scale_dtype == SMOE_SCALE_F32
+               ? gm_dispatch<float>(L.desc.bits, A, false, GV_F32, grid, lds, stream)
+               : gm_dispatch<_Float16>(L.desc.bits, A, false, GV_F32, grid, lds, stream);
   grouped_shape(P.down, false, shared ? 1 : max_slots, A, grid, lds);
   const int v = P.down.v;
   if (L.desc.bits == 4)
