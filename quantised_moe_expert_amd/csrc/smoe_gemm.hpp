@@ -34,7 +34,7 @@
 #include "smoe_launch.hpp"
 
 #ifndef SMOE_GM_GB
-#define SMOE_GM_GB (GU ? 4 : 8)
+#define SMOE_GM_GB 8
 #endif
 
 
@@ -164,36 +164,19 @@ __device__ __forceinline__ h8 gm_operand(uint32_t w, int h, uint32_t magic) {
   return __builtin_bit_cast(h8, t);
 }
 
-// Scales of groups g0 .. g0 + 3 of one row. SV: the row holds a multiple of
-// four groups and g0 is a multiple of four (one vector load; a quad past the
-// row is read from the row's last quad); else one load per group, clamped to
-// the row. The caller zeroes the scales of groups it does not own.
-template <typename ST, bool SV>
-__device__ __forceinline__ void gm_scales4(const ST* rs, int g0, int G, float* out) {
-  if constexpr (SV) {
-    const int q = min(g0, G - 4);
-    if constexpr (sizeof(ST) == 4) {
-      const u32x4 t = *(const u32x4_a4*)(rs + q);
-      // components go through named scalars: a bit_cast of a vector
-      // component expression reads component 0
-      const uint32_t t0 = t.x, t1 = t.y, t2 = t.z, t3 = t.w;
-      out[0] = __builtin_bit_cast(float, t0);
-      out[1] = __builtin_bit_cast(float, t1);
-      out[2] = __builtin_bit_cast(float, t2);
-      out[3] = __builtin_bit_cast(float, t3);
-    } else {
-      const u32x2 t = *(const u32x2_a4*)(rs + q);
-      const uint32_t lo = t.x, hi = t.y;
-      const f16x2 a = __builtin_bit_cast(f16x2, lo), c = __builtin_bit_cast(f16x2, hi);
-      const _Float16 a0 = a.x, a1 = a.y, c0 = c.x, c1 = c.y;
-      out[0] = (float)a0;
-      out[1] = (float)a1;
-      out[2] = (float)c0;
-      out[3] = (float)c1;
-    }
+// Four consecutive scales of one row starting at group q (a multiple of
+// four, q + 4 <= G), as float bit patterns.
+template <typename ST>
+__device__ __forceinline__ u32x4 gm_scale_quad(const ST* rs, int q) {
+  if constexpr (sizeof(ST) == 4) {
+    return *(const u32x4_a4*)(rs + q);
   } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = load_scale<ST, false>(rs + min(g0 + j, G - 1));
+    const u32x2 t = *(const u32x2_a4*)(rs + q);
+    const uint32_t lo = t.x, hi = t.y;
+    const f16x2 a = __builtin_bit_cast(f16x2, lo), c = __builtin_bit_cast(f16x2, hi);
+    const _Float16 a0 = a.x, a1 = a.y, c0 = c.x, c1 = c.y;
+    return u32x4{__builtin_bit_cast(uint32_t, (float)a0), __builtin_bit_cast(uint32_t, (float)a1),
+                 __builtin_bit_cast(uint32_t, (float)c0), __builtin_bit_cast(uint32_t, (float)c1)};
   }
 }
 
@@ -293,9 +276,17 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
   const int wmap = BITS == 4 ? (b & 1) * 4 + (b >> 1) * 2 : b;
   constexpr int UG = BITS == 4 ? 2 : 4;  // groups per load unit
   constexpr int NU = GB / UG;             // load units per batch
+  static_assert(GB == 8, "one scale load per lane covers a batch of eight groups");
+  // Scales (SV: every row holds whole quads of groups): one 16-byte load per
+  // lane per batch, quarter b reading quad b & 1 of the batch, of the up
+  // matrix when b >= 2 (gate/up) and a copy of quarters 0, 1 otherwise;
+  // lane swaps broadcast each quad to all quarters at use. Without SV every
+  // lane loads each scale it needs.
+  const ST* sq_row = (GU && (b >> 1)) ? s1 : s0;
   struct Batch {
     u32x4 wa[NU], wb[NU];
-    float sa[GB], sb[GB];
+    u32x4 sq;                     // SV
+    float sa[SV ? 1 : GB], sb[SV ? 1 : GB];  // not SV
   };
   auto load = [&](Batch& B, int g0) {
 #pragma unroll
@@ -303,10 +294,44 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
       B.wa[u] = gm_unit_load<BITS>(c0, g0 + u * UG, G, b);
       if constexpr (GU) B.wb[u] = gm_unit_load<BITS>(c1, g0 + u * UG, G, b);
     }
+    if constexpr (SV) {
+      B.sq = gm_scale_quad<ST>(sq_row, min(g0 + 4 * (b & 1), G - 4));
+    } else {
 #pragma unroll
-    for (int q = 0; q < GB / 4; ++q) {
-      gm_scales4<ST, SV>(s0, g0 + 4 * q, G, B.sa + 4 * q);
-      if constexpr (GU) gm_scales4<ST, SV>(s1, g0 + 4 * q, G, B.sb + 4 * q);
+      for (int j = 0; j < GB; ++j) {
+        B.sa[j] = load_scale<ST, false>(s0 + min(g0 + j, G - 1));
+        if constexpr (GU) B.sb[j] = load_scale<ST, false>(s1 + min(g0 + j, G - 1));
+      }
+    }
+  };
+  // the scales of a batch for this lane's row: sa (gate or the only
+  // matrix), sb (up)
+  auto scales = [&](const Batch& B, float* sa, float* sb) {
+    if constexpr (SV) {
+      uint32_t q[4] = {B.sq.x, B.sq.y, B.sq.z, B.sq.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t lo = q[i], hi = q[i];
+        swap16(lo, hi);  // lo: quarters' quad 0 (gate | up), hi: quad 1
+        if constexpr (GU) {
+          uint32_t lo2 = lo, hi2 = hi;
+          swap32(lo, lo2);  // lo: gate quad 0, lo2: up quad 0
+          swap32(hi, hi2);
+          sa[i] = __builtin_bit_cast(float, lo);
+          sb[i] = __builtin_bit_cast(float, lo2);
+          sa[4 + i] = __builtin_bit_cast(float, hi);
+          sb[4 + i] = __builtin_bit_cast(float, hi2);
+        } else {
+          sa[i] = __builtin_bit_cast(float, lo);
+          sa[4 + i] = __builtin_bit_cast(float, hi);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < GB; ++j) {
+        sa[j] = B.sa[j];
+        if constexpr (GU) sb[j] = B.sb[j];
+      }
     }
   };
   // the word that group j of an arranged batch feeds to MFMA h
@@ -333,6 +358,8 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
     // wave's range) count with scale zero and read the last group's LDS
     auto compute = [&](const Batch& B, int g0) {
       uint32_t wa[NU][4], wb[NU][4];
+      float bsa[GB], bsb[GB];
+      scales(B, bsa, bsb);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         gm_unit_arrange<BITS>(B.wa[u], wa[u]);
@@ -342,7 +369,7 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
       for (int j = 0; j < GB; ++j) {
         const bool own = g0 + j < gb1;  // wave-uniform
         const int g = min(g0 + j, G - 1);
-        const float sa = own ? B.sa[j] : 0.f;
+        const float sa = own ? bsa[j] : 0.f;
         f32x4m da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -371,7 +398,7 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
         acc_a.z = fmaf(sa, a2 - k2, acc_a.z);
         acc_a.w = fmaf(sa, a3 - k3, acc_a.w);
         if constexpr (GU) {
-          const float sb = own ? B.sb[j] : 0.f;
+          const float sb = own ? bsb[j] : 0.f;
           const float b0 = db.x, b1 = db.y, b2 = db.z, b3 = db.w;
           acc_b.x = fmaf(sb, b0 - k0, acc_b.x);
           acc_b.y = fmaf(sb, b1 - k1, acc_b.y);

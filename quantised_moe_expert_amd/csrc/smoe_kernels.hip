@@ -277,13 +277,13 @@ static void grouped_shape(const MatPlan& m, bool split, int slots, GemvArgs& A, 
 // Launch shape of a matrix-core stage: 16-row tiles, one per wave, or one
 // per workgroup with its groups split over the four waves when one tile per
 // wave leaves under 1024 workgroups. Tokens per chunk: twice the mean pairs
-// per slot (at least 4, at most 16, one MFMA's M) so that the LDS a
+// per slot (at least 8, at most 16, one MFMA's M) so that the LDS a
 // workgroup holds stays small enough for several workgroups per CU, then cut
 // to fit 64 KB; slots with more pairs take several chunks. The k-split
 // partial-sum region (last in the layout) is allocated only when used.
 // False when not even one token fits.
 #ifndef SMOE_GM_TC_MIN
-#define SMOE_GM_TC_MIN 4
+#define SMOE_GM_TC_MIN 8
 #endif
 static bool gm_shape(const MatPlan& m, bool split, int pairs, int slots, GemvArgs& A, dim3& grid,
                      unsigned& lds) {
