@@ -250,18 +250,19 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
   if (p0 >= p1) return;  // workgroup-uniform
   const MatArgs& M0 = A.m0;
   const int rows = M0.rows, Wr = M0.words_per_row, G = M0.cols / 64, TC = A.tc;
-  const int ks = A.ksplit;  // waves per 16-row tile: 1 or 4
-  const int tile = wave / ks, kpart = wave - tile * ks;
-  const int row0 = (blockIdx.x * (GV_WAVES / ks) + tile) * 16;
+  const int ks = A.ksplit;           // waves per 16-row tile: 1 or 4
+  const int tpw = A.tiles_per_wave;  // tiles a wave takes in turn (1 with the k-split)
+  const int tw = wave / ks, kpart = wave - tw * ks;
   const int r = lane & 15, b = lane >> 4;
-  const int row = row0 + r, rc = row < rows ? row : rows - 1;
   const int gper = ((G + ks - 1) / ks + 3) & ~3;  // a multiple of four groups
   const int gb0 = min(G, kpart * gper), gb1 = min(G, gb0 + gper);
+  const int nbt = (gb1 - gb0 + GB - 1) / GB;  // batches per tile (0: an empty k-part)
+  const int nb = nbt * tpw;                   // batches of this wave per chunk
   const uint8_t* blob = A.blobs + (uint64_t)e * A.stride;
-  const uint32_t* c0 = (const uint32_t*)(blob + M0.codes_off) + (size_t)rc * Wr;
-  const ST* s0 = (const ST*)(blob + M0.scales_off) + (size_t)rc * G;
-  const uint32_t* c1 = (const uint32_t*)(blob + A.m1.codes_off) + (size_t)rc * Wr;
-  const ST* s1 = (const ST*)(blob + A.m1.scales_off) + (size_t)rc * G;
+  const uint32_t* cm0 = (const uint32_t*)(blob + M0.codes_off);
+  const ST* sm0 = (const ST*)(blob + M0.scales_off);
+  const uint32_t* cm1 = (const uint32_t*)(blob + A.m1.codes_off);
+  const ST* sm1 = (const ST*)(blob + A.m1.scales_off);
   constexpr bool SPLIT = IN == GV_F32_SPLIT;
   const GmLds L = gm_lds_layout(M0.cols, TC, SPLIT);
   const uint32_t* X = lds + L.x;
@@ -277,30 +278,49 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
   constexpr int UG = BITS == 4 ? 2 : 4;  // groups per load unit
   constexpr int NU = GB / UG;             // load units per batch
   static_assert(GB == 8, "one scale load per lane covers a batch of eight groups");
+
+  // Batch k of the wave: tile item k / nbt (consecutive waves of a workgroup
+  // take consecutive tiles), groups gb0 + (k % nbt) * GB onwards. Batches
+  // past the wave's last are read from its last tile, past its groups
+  // (clamped: cache hits, never used).
+  struct Pos {
+    int t, g0;
+  };
+  auto pos = [&](int k) -> Pos {
+    const int t = min(k / max(nbt, 1), tpw - 1);
+    return Pos{t, gb0 + (k - t * nbt) * GB};
+  };
+  auto row_of = [&](int t) { return ((blockIdx.x * tpw + t) * (GV_WAVES / ks) + tw) * 16 + r; };
+
   // Scales (SV: every row holds whole quads of groups): one 16-byte load per
   // lane per batch, quarter b reading quad b & 1 of the batch, of the up
   // matrix when b >= 2 (gate/up) and a copy of quarters 0, 1 otherwise;
   // lane swaps broadcast each quad to all quarters at use. Without SV every
   // lane loads each scale it needs.
-  const ST* sq_row = (GU && (b >> 1)) ? s1 : s0;
   struct Batch {
     u32x4 wa[NU], wb[NU];
-    u32x4 sq;                     // SV
+    u32x4 sq;                                // SV
     float sa[SV ? 1 : GB], sb[SV ? 1 : GB];  // not SV
   };
-  auto load = [&](Batch& B, int g0) {
+  auto load = [&](Batch& B, int k) {
+    const Pos P = pos(k);
+    const int rc = min(row_of(P.t), rows - 1);
+    const uint32_t* c0 = cm0 + (size_t)rc * Wr;
+    const uint32_t* c1 = cm1 + (size_t)rc * Wr;
+    const ST* s0 = sm0 + (size_t)rc * G;
+    const ST* s1 = sm1 + (size_t)rc * G;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      B.wa[u] = gm_unit_load<BITS>(c0, g0 + u * UG, G, b);
-      if constexpr (GU) B.wb[u] = gm_unit_load<BITS>(c1, g0 + u * UG, G, b);
+      B.wa[u] = gm_unit_load<BITS>(c0, P.g0 + u * UG, G, b);
+      if constexpr (GU) B.wb[u] = gm_unit_load<BITS>(c1, P.g0 + u * UG, G, b);
     }
     if constexpr (SV) {
-      B.sq = gm_scale_quad<ST>(sq_row, min(g0 + 4 * (b & 1), G - 4));
+      B.sq = gm_scale_quad<ST>((GU && (b >> 1)) ? s1 : s0, min(P.g0 + 4 * (b & 1), G - 4));
     } else {
 #pragma unroll
       for (int j = 0; j < GB; ++j) {
-        B.sa[j] = load_scale<ST, false>(s0 + min(g0 + j, G - 1));
-        if constexpr (GU) B.sb[j] = load_scale<ST, false>(s1 + min(g0 + j, G - 1));
+        B.sa[j] = load_scale<ST, false>(s0 + min(P.g0 + j, G - 1));
+        if constexpr (GU) B.sb[j] = load_scale<ST, false>(s1 + min(P.g0 + j, G - 1));
       }
     }
   };
@@ -341,12 +361,12 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
   };
 
   Batch bA, bB;
-  load(bA, gb0);  // in flight while the tokens are staged
+  load(bA, 0);  // in flight while the tokens are staged
   for (int pc = p0; pc < p1; pc += TC) {
     const int nt = min(TC, p1 - pc);
     if (pc > p0) {
       __syncthreads();  // the previous chunk's readers are done
-      load(bA, gb0);
+      load(bA, 0);
     }
     gm_stage<BITS, IN, GU>(A, M0, lds, L, pc, nt);
     // A row r of the MFMAs is token r; rows past the chunk read whatever the
@@ -354,9 +374,14 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
     // never used
     const int rr = min(r, TC - 1);
     f32x4m acc_a = {0.f, 0.f, 0.f, 0.f}, acc_b = {0.f, 0.f, 0.f, 0.f};
-    // groups g0 .. g0 + GB - 1; those at or past gb1 (the tail of the
-    // wave's range) count with scale zero and read the last group's LDS
-    auto compute = [&](const Batch& B, int g0) {
+    // batch k; groups at or past gb1 (the tail of the wave's range) count
+    // with scale zero and read the last group's LDS
+    auto compute = [&](const Batch& B, int k) {
+      const int g0 = pos(k).g0;
+      if (g0 == gb0) {  // a new tile
+        acc_a = f32x4m{0.f, 0.f, 0.f, 0.f};
+        acc_b = f32x4m{0.f, 0.f, 0.f, 0.f};
+      }
       uint32_t wa[NU][4], wb[NU][4];
       float bsa[GB], bsb[GB];
       scales(B, bsa, bsb);
@@ -407,29 +432,61 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
         }
       }
     };
-    // Loads are unconditional (past the row they re-read its last group, a
-    // cache hit) so that the number in flight is the same on every path and
-    // each wait covers exactly the batch about to be used.
+    // the outputs of tile item t: tokens 4b .. 4b + 3 of row r
+    auto store = [&](int t, const float* va, const float* vb) {
+      const int row = row_of(t);
+      if (kpart == 0 && row < rows) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tk = 4 * b + i;
+          if (tk < nt) {
+            const float o = osc[tk];
+            float val;
+            if constexpr (GU) {
+              const float gg = va[i] * o, uu = vb[i] * o;
+              val = gg / (1.0f + expf(-gg)) * uu;
+            } else {
+              val = va[i] * o;
+            }
+            A.out[(size_t)(pc + tk) * rows + row] = val;
+          }
+        }
+      }
+    };
+    auto finish_tile = [&](int k) {  // after batch k, without the k-split
+      if (ks == 1 && k - pos(k).t * nbt == nbt - 1) {
+        const float va[4] = {acc_a.x, acc_a.y, acc_a.z, acc_a.w};
+        const float vb[4] = {acc_b.x, acc_b.y, acc_b.z, acc_b.w};
+        store(pos(k).t, va, vb);
+      }
+    };
+    // Loads are unconditional (past the wave's work they re-read its last
+    // groups, cache hits) so that the number in flight is the same on every
+    // path and each wait covers exactly the batch about to be used.
     // Scheduling barriers keep each batch's loads ahead of the computation
     // on the other batch (the scheduler would otherwise sink them past it).
-    for (int g0 = gb0; g0 < gb1; g0 += 2 * GB) {
-      load(bB, g0 + GB);
+    for (int k = 0; k < nb; k += 2) {
+      load(bB, k + 1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(bA, g0);
+      compute(bA, k);
+      finish_tile(k);
       __builtin_amdgcn_sched_barrier(0);
-      load(bA, g0 + 2 * GB);
+      load(bA, k + 2);
       __builtin_amdgcn_sched_barrier(0);
-      if (g0 + GB < gb1) compute(bB, g0 + GB);
+      if (k + 1 < nb) {
+        compute(bB, k + 1);
+        finish_tile(k + 1);
+      }
     }
-    // partial sums of the k-split waves meet in LDS
-    float va[4] = {acc_a.x, acc_a.y, acc_a.z, acc_a.w};
-    float vb[4] = {acc_b.x, acc_b.y, acc_b.z, acc_b.w};
     if (ks > 1) {
+      // partial sums of the k-split waves meet in LDS (one tile per wave)
+      float va[4] = {acc_a.x, acc_a.y, acc_a.z, acc_a.w};
+      float vb[4] = {acc_b.x, acc_b.y, acc_b.z, acc_b.w};
       if (kpart > 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          part[((tile * 4 + kpart) * 64 + lane) * 8 + i] = va[i];
-          part[((tile * 4 + kpart) * 64 + lane) * 8 + 4 + i] = vb[i];
+          part[((tw * 4 + kpart) * 64 + lane) * 8 + i] = va[i];
+          part[((tw * 4 + kpart) * 64 + lane) * 8 + 4 + i] = vb[i];
         }
       }
       __syncthreads();
@@ -437,27 +494,11 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
         for (int kp = 1; kp < ks; ++kp)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            va[i] += part[((tile * 4 + kp) * 64 + lane) * 8 + i];
-            vb[i] += part[((tile * 4 + kp) * 64 + lane) * 8 + 4 + i];
+            va[i] += part[((tw * 4 + kp) * 64 + lane) * 8 + i];
+            vb[i] += part[((tw * 4 + kp) * 64 + lane) * 8 + 4 + i];
           }
       }
-    }
-    if (kpart == 0 && row < rows) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * b + i;
-        if (t < nt) {
-          const float o = osc[t];
-          float val;
-          if constexpr (GU) {
-            const float gg = va[i] * o, uu = vb[i] * o;
-            val = gg / (1.0f + expf(-gg)) * uu;
-          } else {
-            val = va[i] * o;
-          }
-          A.out[(size_t)(pc + t) * rows + row] = val;
-        }
-      }
+      store(0, va, vb);
     }
   }
 }

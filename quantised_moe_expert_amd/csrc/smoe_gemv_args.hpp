@@ -73,6 +73,7 @@ struct GemvArgs {
   int rows_per_wave;     // a multiple of the rows one wave covers per step
   int tc;                // tokens staged in LDS per chunk
   int ksplit;            // matrix-core stage: waves sharing one 16-row tile
+  int tiles_per_wave;    // matrix-core stage: tiles each wave takes in turn
   const void* x;         // activations: gate/up: [T, cols]; down: h [pairs, cols]
   int x_ld;              // elements between consecutive activation vectors
   int rms;               // gate/up: apply unit-gain RMSNorm to x

@@ -282,6 +282,9 @@ static void grouped_shape(const MatPlan& m, bool split, int slots, GemvArgs& A, 
 // to fit 64 KB; slots with more pairs take several chunks. The k-split
 // partial-sum region (last in the layout) is allocated only when used.
 // False when not even one token fits.
+#ifndef SMOE_GM_TPW_MAX
+#define SMOE_GM_TPW_MAX 4
+#endif
 #ifndef SMOE_GM_TC_MIN
 #define SMOE_GM_TC_MIN 8
 #endif
@@ -291,7 +294,15 @@ static bool gm_shape(const MatPlan& m, bool split, int pairs, int slots, GemvArg
   const int ks = (int64_t)(tiles + GV_WAVES - 1) / GV_WAVES * slots < 1024 ? GV_WAVES : 1;
   A.ksplit = ks;
   const int tpb = GV_WAVES / ks;
-  grid = dim3((tiles + tpb - 1) / tpb, slots);
+  // tiles per wave: more while the grid keeps over 1024 workgroups, so that
+  // each staging of the tokens serves more rows
+  int tpw = 1;
+  if (ks == 1)
+    while (tpw < SMOE_GM_TPW_MAX &&
+           (int64_t)((tiles + tpb * 2 * tpw - 1) / (tpb * 2 * tpw)) * slots >= 1024)
+      tpw *= 2;
+  A.tiles_per_wave = tpw;
+  grid = dim3((tiles + tpb * tpw - 1) / (tpb * tpw), slots);
   const int mean = (pairs + slots - 1) / slots;
   int tc = 2 * mean < SMOE_GM_TC_MIN ? SMOE_GM_TC_MIN : (2 * mean > 16 ? 16 : 2 * mean);
   auto bytes = [&](int t) {
