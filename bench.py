@@ -278,7 +278,7 @@ def main():
 
 KERNEL_SOURCES = {
     "gate_up": ("smoe_decode.hpp", "smoe_decode_args.hpp", "smoe_device.hpp"),
-    "gate_up_grouped": ("smoe_gemv.hpp", "smoe_gemv_args.hpp", "smoe_device.hpp"),
+    "gate_up_grouped": ("smoe_gemm.hpp", "smoe_gemv.hpp", "smoe_gemv_args.hpp", "smoe_device.hpp"),
 }
 
 
