@@ -11,14 +11,13 @@
 namespace smoe {
 
 // ------------------------------------------------------------ route+group --
-// One workgroup. Phase A: a wave per token selects the top-k (descending
-// logit, ties to the lower id) and the softmax-over-all weights
-// ("CMF v2 Format Specification", 2.2). Phase B (optional) groups the
-// (token, slot) pairs by expert: active experts ascending, and inside an
-// expert the pairs in ascending token order, so the grouping is unique.
+// k_topk: a wave per token selects the top-k (descending logit, ties to the
+// lower id) and the softmax-over-all weights ("CMF v2 Format Specification",
+// 2.2), tokens spread over the whole grid (the k rounds are VALU work, too
+// much for one CU at a few dozen tokens). k_group (optional, one workgroup)
+// then groups the (token, slot) pairs by expert.
 
-constexpr int ROUTE_THREADS = 1024;
-constexpr int ROUTE_EPL = SMOE_MAX_EXPERTS / 64;  // logits per lane
+static_assert(SMOE_MAX_EXPERTS <= 512, "top-k kernels hold at most 8 logits per lane");
 
 struct RouteArgs {
   const float* logits;
@@ -34,82 +33,166 @@ struct RouteArgs {
   int* pair_of;
 };
 
-__global__ __launch_bounds__(ROUTE_THREADS) void k_route(RouteArgs A) {
-  extern __shared__ uint32_t lds[];
-  const int TW = (A.T + 31) >> 5;
-  uint32_t* sel = lds;                          // [E][TW] token bitmask per expert
-  int* slot_of = (int*)(lds + A.E * TW);        // [E]
-  int* cnt = slot_of + A.E;                     // [E]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nwaves = blockDim.x >> 6;
-  if (A.group) {
-    for (int i = tid; i < A.E * TW; i += blockDim.x) sel[i] = 0u;
-    __syncthreads();
-  }
-  for (int t = wave; t < A.T; t += nwaves) {
+// Selection key of expert e with logit f: unsigned order of the keys is the
+// selection order (larger logit first, -0 equal to +0, equal logits in
+// ascending id); every key is distinct and above 0, the padding key.
+__device__ __forceinline__ uint64_t rt_key(float f, int e) {
+  const int b = __builtin_bit_cast(int, f + 0.0f);
+  const uint32_t o = (uint32_t)(b >= 0 ? b : b ^ 0x7FFFFFFF) ^ 0x80000000u;
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ int rt_key_id(uint64_t k) {
+  return (int)(0xFFFFFFFFu - (uint32_t)k);
+}
+__device__ __forceinline__ float rt_key_logit(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32) ^ 0x80000000u;
+  const int b = (int)o >= 0 ? (int)o : (int)(o ^ 0x7FFFFFFFu);
+  return __builtin_bit_cast(float, b);
+}
+
+// Wave-wide reductions through DPP row operations (the result in every lane).
+template <int CTRL, int RMASK>
+__device__ __forceinline__ uint32_t rt_dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, RMASK, 0xF, false);
+}
+__device__ __forceinline__ uint64_t rt_max64_step(uint64_t v, uint32_t hi, uint32_t lo) {
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+#define RT_STEP64(CTRL, RMASK)                                                    \
+  v = rt_max64_step(v, rt_dpp<CTRL, RMASK>((uint32_t)(v >> 32)),                  \
+                    rt_dpp<CTRL, RMASK>((uint32_t)v))
+__device__ __forceinline__ uint64_t rt_wave_max_key(uint64_t v) {
+  // keys are above 0, so the 0 that rows outside a broadcast's mask receive
+  // never wins
+  RT_STEP64(0xB1, 0xF);   // quad_perm [1,0,3,2]
+  RT_STEP64(0x4E, 0xF);   // quad_perm [2,3,0,1]
+  RT_STEP64(0x141, 0xF);  // row_half_mirror
+  RT_STEP64(0x140, 0xF);  // row_mirror
+  RT_STEP64(0x142, 0xA);  // row_bcast15
+  RT_STEP64(0x143, 0xC);  // row_bcast31
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+#undef RT_STEP64
+// Float max / sum over the wave: the same DPP steps; lanes outside a row
+// broadcast's mask take 0, which can only spoil rows 0 and 2, never lane 63
+// (whose value is returned).
+template <int CTRL, int RMASK>
+__device__ __forceinline__ float rt_dppf(float v) {
+  return __builtin_bit_cast(float, (int)rt_dpp<CTRL, RMASK>(__builtin_bit_cast(uint32_t, v)));
+}
+__device__ __forceinline__ float rt_lane63(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float rt_wave_max(float v) {
+  v = fmaxf(v, rt_dppf<0xB1, 0xF>(v));
+  v = fmaxf(v, rt_dppf<0x4E, 0xF>(v));
+  v = fmaxf(v, rt_dppf<0x141, 0xF>(v));
+  v = fmaxf(v, rt_dppf<0x140, 0xF>(v));
+  v = fmaxf(v, rt_dppf<0x142, 0xA>(v));
+  v = fmaxf(v, rt_dppf<0x143, 0xC>(v));
+  return rt_lane63(v);
+}
+__device__ __forceinline__ float rt_wave_sum(float v) {
+  v += rt_dppf<0xB1, 0xF>(v);
+  v += rt_dppf<0x4E, 0xF>(v);
+  v += rt_dppf<0x141, 0xF>(v);
+  v += rt_dppf<0x140, 0xF>(v);
+  v += rt_dppf<0x142, 0xA>(v);
+  v += rt_dppf<0x143, 0xC>(v);
+  return rt_lane63(v);
+}
+
+// Top-k of one token per wave, over as many workgroups as tokens need:
+// EPL = logits per lane (E <= 64 * EPL).
+constexpr int TOPK_THREADS = 256;
+
+template <int EPL>
+__global__ __launch_bounds__(TOPK_THREADS) void k_topk(RouteArgs A) {
+  const int lane = threadIdx.x & 63;
+  const int gw = (int)(blockIdx.x * (TOPK_THREADS / 64) + (threadIdx.x >> 6));
+  const int nw = (int)(gridDim.x * (TOPK_THREADS / 64));
+  for (int t = gw; t < A.T; t += nw) {
     const float* lg = A.logits + (size_t)t * A.E;
-    float v[ROUTE_EPL];
-    bool valid[ROUTE_EPL];
+    // this lane's logits as distinct selection keys (see rt_key); padding 0.
+    // All loads unconditional (lanes past E re-read the last logit): a load
+    // inside a branch would make the compiler wait for it at the join.
+    float lv[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) lv[i] = lg[min(lane + 64 * i, A.E - 1)];
+    uint64_t key[EPL];
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < ROUTE_EPL; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      valid[i] = e < A.E;
-      float x = valid[i] ? lg[e] : -INFINITY;
+      float x = e < A.E ? lv[i] : -INFINITY;
       if (x != x) x = -INFINITY;  // NaN never outranks a number
-      v[i] = x;
+      key[i] = e < A.E ? rt_key(x, e) : 0;
       mx = fmaxf(mx, x);
     }
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    mx = rt_wave_max(mx);
     float se = 0.f;
 #pragma unroll
-    for (int i = 0; i < ROUTE_EPL; ++i)
-      if (valid[i]) se += expf(v[i] - mx);
-    for (int o = 32; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+    for (int i = 0; i < EPL; ++i)
+      if (key[i]) se += expf(rt_key_logit(key[i]) - mx);
+    se = rt_wave_sum(se);
+    // k rounds: the largest remaining key over the wave wins and its owner
+    // drops it
     float wsum = 0.f;
     float wj[SMOE_MAX_TOP_K];
     int idj[SMOE_MAX_TOP_K];
-    for (int j = 0; j < A.k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i) {
-        const int e = lane + 64 * i;
-        if (valid[i] && (v[i] > bv || (v[i] == bv && e < bi))) {
-          bv = v[i];
-          bi = e;
-        }
-      }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      // remove the winner from its owner's candidates
+    for (int j = 0; j < SMOE_MAX_TOP_K; ++j) {
+      if (j < A.k) {
+        uint64_t best = 0;
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i)
-        if (lane + 64 * i == bi) valid[i] = false;
-      const float p = expf(bv - mx) / se;
-      wj[j] = p;
-      idj[j] = bi;
-      wsum += p;
+        for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+        best = rt_wave_max_key(best);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (key[i] == best) key[i] = 0;
+        const float p = expf(rt_key_logit(best) - mx) / se;
+        wj[j] = p;
+        idj[j] = rt_key_id(best);
+        wsum += p;
+      }
     }
-    if (lane == 0) {
-      for (int j = 0; j < A.k; ++j) {
+    // lane j < k writes selection j
+#pragma unroll
+    for (int j = 0; j < SMOE_MAX_TOP_K; ++j) {
+      if (j < A.k && lane == j) {
         const float wt = A.norm ? wj[j] / wsum : wj[j];
         const size_t o = (size_t)t * A.k + j;
         A.ids[o] = idj[j];
         A.w[o] = wt;
         if (A.user_ids) A.user_ids[o] = idj[j];
         if (A.user_w) A.user_w[o] = wt;
-        if (A.group) atomicOr(&sel[idj[j] * TW + (t >> 5)], 1u << (t & 31));
       }
     }
   }
-  if (!A.group) return;
+}
+
+// Grouping of the T*k (token, slot) pairs by expert, one workgroup: active
+// experts ascending, and inside an expert the pairs in ascending token order,
+// so the grouping is unique.
+constexpr int GROUP_THREADS = 1024;
+
+__global__ __launch_bounds__(GROUP_THREADS) void k_group(RouteArgs A) {
+  extern __shared__ uint32_t lds[];
+  const int TW = (A.T + 31) >> 5;
+  uint32_t* sel = lds;                          // [E][TW] token bitmask per expert
+  int* slot_of = (int*)(lds + A.E * TW);        // [E]
+  int* cnt = slot_of + A.E;                     // [E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = A.T * A.k;
+  for (int i = tid; i < A.E * TW; i += blockDim.x) sel[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < P; i += blockDim.x) {
+    const int t = i / A.k;
+    atomicOr(&sel[A.ids[i] * TW + (t >> 5)], 1u << (t & 31));
+  }
   __syncthreads();
   for (int e = tid; e < A.E; e += blockDim.x) {
     int c = 0;
@@ -148,7 +231,6 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_route(RouteArgs A) {
     }
   }
   __syncthreads();
-  const int P = A.T * A.k;
   for (int i = tid; i < P; i += blockDim.x) {
     const int t = i / A.k;
     const int e = A.ids[i];
@@ -168,12 +250,22 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int3
                         hipStream_t stream) {
   RouteArgs A{logits, T, E, k, norm, group, ids, w, user_ids, user_w,
               meta, active, offs, pair_token, pair_of};
+  const int tpb = TOPK_THREADS / 64;
+  int blocks = (T + tpb - 1) / tpb;
+  blocks = blocks > 1024 ? 1024 : blocks;
+  const dim3 grid(blocks), block(TOPK_THREADS);
+  if (E <= 64)
+    hipLaunchKernelGGL(k_topk<1>, grid, block, 0, stream, A);
+  else if (E <= 128)
+    hipLaunchKernelGGL(k_topk<2>, grid, block, 0, stream, A);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_topk<4>, grid, block, 0, stream, A);
+  else
+    hipLaunchKernelGGL(k_topk<8>, grid, block, 0, stream, A);
+  if (!group) return hipGetLastError();
   const int TW = (T + 31) / 32;
-  const size_t lds = group ? (size_t)E * TW * 4 + (size_t)E * 8 : 0;
-  int threads = T * 64;
-  if (threads > ROUTE_THREADS) threads = ROUTE_THREADS;
-  if (threads < 256 && group) threads = 256;
-  hipLaunchKernelGGL(k_route, dim3(1), dim3(threads), lds, stream, A);
+  const size_t lds = (size_t)E * TW * 4 + (size_t)E * 8;
+  hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), lds, stream, A);
   return hipGetLastError();
 }
 
