@@ -76,7 +76,7 @@ extern "C" {
 #define SMOE_BLOB_ALIGN 16384    /* blob stride granularity                   */
 #define SMOE_MAX_TOP_K 16        /* routing width cap                         */
 #define SMOE_MAX_EXPERTS 512     /* routed experts per layer                  */
-#define SMOE_MAX_TOKENS 1024     /* tokens per smoe_moe_forward call          */
+#define SMOE_MAX_TOKENS 4096     /* tokens per smoe_moe_forward call          */
 #define SMOE_BANK_ALIGN 256      /* required alignment of blob base pointers  */
 
 /* Description of one MoE layer's expert bank. */
@@ -144,7 +144,7 @@ int smoe_load_blobs(const smoe_layer_desc* desc, const void* d_blobs, uint64_t n
 void smoe_free(smoe_layer* layer);
 
 /* Bytes of device workspace smoe_moe_forward needs for n_tokens tokens and
- * top_k (0 on invalid arguments). smoe_decode_step needs the same amount for
+ * top_k (0 on invalid arguments or a batch the grouping cannot hold). smoe_decode_step needs the same amount for
  * the largest layer it runs. Calls that share a workspace must be ordered
  * (one stream, or synchronised). */
 uint64_t smoe_workspace_bytes(const smoe_layer* layer, int n_tokens, int top_k);
@@ -174,7 +174,10 @@ int smoe_route(const float* d_logits, int n_tokens, int n_experts, int top_k,
  *  d_workspace at least smoe_workspace_bytes(layer, n_tokens, top_k) bytes,
  *             256-byte aligned; contents are scratch and need no clearing.
  * Tokens that share an expert read its weights once per call.
- * Errors: SMOE_E_ARG, SMOE_E_WORKSPACE, SMOE_E_HIP. n_tokens == 0 is a no-op.
+ * Errors: SMOE_E_ARG, SMOE_E_WORKSPACE, SMOE_E_UNSUPPORTED (the per-expert
+ * token bitmasks of the grouping, num_experts * ceil(n_tokens / 32) * 4 +
+ * num_experts * 8 bytes, exceed 160 KB: e.g. more than ~2400 tokens with 512
+ * experts), SMOE_E_HIP. n_tokens == 0 is a no-op.
  * Activations must be finite with |x| < 2^100 (they are rescaled by a power
  * of two per vector before the fp16 dot products). */
 int smoe_moe_forward(const smoe_layer* layer, const void* d_x, int x_dtype,

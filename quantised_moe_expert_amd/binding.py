@@ -32,7 +32,7 @@ SMOE_SCALE_F16 = 1
 
 SMOE_MAX_TOP_K = 16
 SMOE_MAX_EXPERTS = 512
-SMOE_MAX_TOKENS = 1024
+SMOE_MAX_TOKENS = 4096
 
 SMOE_KERNEL_NONE = 0
 SMOE_KERNEL_GATE_UP = 1

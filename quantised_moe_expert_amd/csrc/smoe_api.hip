@@ -278,7 +278,7 @@ void smoe_free(smoe_layer* layer) { delete layer; }
 
 uint64_t smoe_workspace_bytes(const smoe_layer* layer, int n_tokens, int top_k) {
   if (!layer || n_tokens < 0 || n_tokens > SMOE_MAX_TOKENS || top_k < 1 ||
-      top_k > SMOE_MAX_TOP_K)
+      top_k > SMOE_MAX_TOP_K || !group_fits((int)layer->info.desc.num_experts, n_tokens))
     return 0;
   return ws_layout(layer->info, n_tokens, top_k).total;
 }
@@ -309,12 +309,10 @@ static int check_forward_args(const smoe_layer* layer, int n_tokens, int top_k,
   const int kmax = E < SMOE_MAX_TOP_K ? E : SMOE_MAX_TOP_K;
   if (top_k < 1 || top_k > kmax)
     return fail(SMOE_E_ARG, "top_k must be in [1, %d] (got %d)", kmax, top_k);
+  if (!group_fits(E, n_tokens))
+    return fail(SMOE_E_UNSUPPORTED, "%d tokens over %d experts exceed the grouping's LDS", n_tokens,
+                E);
   if (n_tokens == 0) return SMOE_OK;
-  // the grouping step keeps an expert x token bitmask in LDS (<= 64 KB)
-  const uint64_t lds = (uint64_t)E * ((n_tokens + 31) / 32) * 4 + (uint64_t)E * 8;
-  if (lds > 65536)
-    return fail(SMOE_E_UNSUPPORTED, "%d experts x %d tokens exceed the grouping limit", E,
-                n_tokens);
   const uint64_t need = ws_layout(layer->info, n_tokens, top_k).total;
   if (!d_workspace || ws_bytes < need)
     return fail(SMOE_E_WORKSPACE, "workspace of %llu bytes needed (got %llu)",

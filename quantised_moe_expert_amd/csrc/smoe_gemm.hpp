@@ -44,12 +44,13 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f32x4m __attribute__((ext_vector_type(4)));
 
 // Stage pairs [pc, pc + nt) of the slot for the matrix-core stage.
-template <int BITS, int IN, bool GU>
+template <int BITS, int IN, bool GU, int NW>
 __device__ __forceinline__ void gm_stage(const GemvArgs& A, const MatArgs& M, uint32_t* lds,
                                          const GmLds& L, int pc, int nt) {
   constexpr int WPW = QT<BITS>::WPW, PPW = QT<BITS>::PPW, NPOS = QT<BITS>::NPOS;
   constexpr int WPG = QT<BITS>::WPG;  // words per group
   constexpr bool XF32 = IN != GV_BF16, SPLIT = IN == GV_F32_SPLIT;
+  constexpr int NT = NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cols = M.cols, Wr = M.words_per_row, G = cols / 64, TC = A.tc;
   const size_t esz = XF32 ? 4 : 2;
@@ -62,7 +63,7 @@ __device__ __forceinline__ void gm_stage(const GemvArgs& A, const MatArgs& M, ui
   for (int i = 0; i < nt; ++i) {
     const void* v = vec(i);
     float amax = 0.f, ss = 0.f;
-    for (int cw = tid; cw < Wr; cw += GV_THREADS) {
+    for (int cw = tid; cw < Wr; cw += NT) {
       float xv[WPW];
       gv_load_word<BITS, XF32>(v, cw, xv);
 #pragma unroll
@@ -74,8 +75,8 @@ __device__ __forceinline__ void gm_stage(const GemvArgs& A, const MatArgs& M, ui
     amax = lane63(seg_max(amax, 6));
     ss = lane63(seg_sum(ss, 6));
     if (lane == 0) {
-      red[(i * GV_WAVES + wave) * 2] = amax;
-      red[(i * GV_WAVES + wave) * 2 + 1] = ss;
+      red[(i * NW + wave) * 2] = amax;
+      red[(i * NW + wave) * 2 + 1] = ss;
     }
   }
   __syncthreads();
@@ -87,13 +88,13 @@ __device__ __forceinline__ void gm_stage(const GemvArgs& A, const MatArgs& M, ui
   // X[((cw * HALVES + hv) * TC + i) * 4 + (q % 4)] with hv = q / 4 (split
   // inputs: the hi halves there, the lo halves at the same place in Xlo)
   constexpr int HALVES = PPW / 4;
-  for (int u = tid; u < G * nt; u += GV_THREADS) {
+  for (int u = tid; u < G * nt; u += NT) {
     const int i = u / G, g = u - i * G;
     float m = 0.f, q2 = 0.f;
 #pragma unroll
-    for (int w = 0; w < GV_WAVES; ++w) {
-      m = fmaxf(m, red[(i * GV_WAVES + w) * 2]);
-      q2 += red[(i * GV_WAVES + w) * 2 + 1];
+    for (int w = 0; w < NW; ++w) {
+      m = fmaxf(m, red[(i * NW + w) * 2]);
+      q2 += red[(i * NW + w) * 2 + 1];
     }
     int ex = 0;
     frexpf(m, &ex);
@@ -131,7 +132,7 @@ __device__ __forceinline__ void gm_stage(const GemvArgs& A, const MatArgs& M, ui
     Kl[g * 16 + i] = kk;
   }
   // K of the token rows past the chunk (their D rows are never used)
-  for (int u = tid; u < G * 16; u += GV_THREADS)
+  for (int u = tid; u < G * 16; u += NT)
     if ((u & 15) >= nt) Kl[u] = 0.f;
   __syncthreads();
 }
@@ -228,8 +229,8 @@ __device__ __forceinline__ void gm_unit_arrange(const u32x4& t, uint32_t w[4]) {
   }
 }
 
-template <int BITS, typename ST, int IN, bool GU, bool SV>
-__global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
+template <int BITS, typename ST, int IN, bool GU, bool SV, int NW>
+__global__ __launch_bounds__(NW * 64) void k_gemm(GemvArgs A) {
   extern __shared__ uint32_t lds[];
   constexpr int WPG = QT<BITS>::WPG, HALVES = QT<BITS>::PPW / 4;
   constexpr int GB = SMOE_GM_GB;  // groups per load batch (multiple of 4)
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
   if (p0 >= p1) return;  // workgroup-uniform
   const MatArgs& M0 = A.m0;
   const int rows = M0.rows, Wr = M0.words_per_row, G = M0.cols / 64, TC = A.tc;
-  const int ks = A.ksplit;           // waves per 16-row tile: 1 or 4
+  const int ks = A.ksplit;           // waves per 16-row tile: 1 or 4 (4 only with NW = 4)
   const int tpw = A.tiles_per_wave;  // tiles a wave takes in turn (1 with the k-split)
   const int tw = wave / ks, kpart = wave - tw * ks;
   const int r = lane & 15, b = lane >> 4;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
   const uint32_t* cm1 = (const uint32_t*)(blob + A.m1.codes_off);
   const ST* sm1 = (const ST*)(blob + A.m1.scales_off);
   constexpr bool SPLIT = IN == GV_F32_SPLIT;
-  const GmLds L = gm_lds_layout(M0.cols, TC, SPLIT);
+  const GmLds L = gm_lds_layout(M0.cols, TC, SPLIT, NW);
   const uint32_t* X = lds + L.x;
   const uint32_t* Xlo = lds + L.xlo;
   const float* Kl = (const float*)(lds + L.k);
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
     const int t = min(k / max(nbt, 1), tpw - 1);
     return Pos{t, gb0 + (k - t * nbt) * GB};
   };
-  auto row_of = [&](int t) { return ((blockIdx.x * tpw + t) * (GV_WAVES / ks) + tw) * 16 + r; };
+  auto row_of = [&](int t) { return ((blockIdx.x * tpw + t) * (NW / ks) + tw) * 16 + r; };
 
   // Scales (SV: every row holds whole quads of groups): one 16-byte load per
   // lane per batch, quarter b reading quad b & 1 of the batch, of the up
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
       __syncthreads();  // the previous chunk's readers are done
       load(bA, 0);
     }
-    gm_stage<BITS, IN, GU>(A, M0, lds, L, pc, nt);
+    gm_stage<BITS, IN, GU, NW>(A, M0, lds, L, pc, nt);
     // A row r of the MFMAs is token r; rows past the chunk read whatever the
     // LDS holds (row TC - 1 past the staged block) and their D rows are
     // never used
@@ -504,23 +505,37 @@ __global__ __launch_bounds__(GV_THREADS) void k_gemm(GemvArgs A) {
 }
 
 // Launcher, instantiated per (BITS, scale type) in smoe_gemm_inst.hip.
-template <int BITS, typename ST, bool SV>
-static hipError_t launch_gm_sv(const GemvArgs& A, bool gate_up, int in, dim3 grid, unsigned lds,
+// Workgroups of more than 64 KB of LDS need the kernel's limit raised.
+template <typename K>
+static hipError_t gm_allow_lds(K kernel, unsigned lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds);
+}
+
+template <int BITS, typename ST, bool SV, int NW>
+static hipError_t launch_gm_nw(const GemvArgs& A, bool gate_up, int in, dim3 grid, unsigned lds,
                                hipStream_t s) {
-  const dim3 block(GV_THREADS);
-  if (!gate_up)
-    return launch_kernel_lds(k_gemm<BITS, ST, GV_F32, false, SV>, grid, block, lds, s, A);
-  if (in == GV_BF16)
-    return launch_kernel_lds(k_gemm<BITS, ST, GV_BF16, true, SV>, grid, block, lds, s, A);
-  return launch_kernel_lds(k_gemm<BITS, ST, GV_F32_SPLIT, true, SV>, grid, block, lds, s, A);
+  const dim3 block(NW * 64);
+  auto go = [&](auto kernel) {
+    const hipError_t e = gm_allow_lds(kernel, lds);
+    return e != hipSuccess ? e : launch_kernel_lds(kernel, grid, block, lds, s, A);
+  };
+  if (!gate_up) return go(k_gemm<BITS, ST, GV_F32, false, SV, NW>);
+  if (in == GV_BF16) return go(k_gemm<BITS, ST, GV_BF16, true, SV, NW>);
+  return go(k_gemm<BITS, ST, GV_F32_SPLIT, true, SV, NW>);
 }
 
 template <int BITS, typename ST>
-hipError_t launch_gm(const GemvArgs& A, bool gate_up, int in, dim3 grid, unsigned lds,
+hipError_t launch_gm(const GemvArgs& A, bool gate_up, int in, int nw, dim3 grid, unsigned lds,
                      hipStream_t s) {
   // vector scale loads when every row holds a whole number of scale quads
-  if (A.m0.cols / 64 % 4 == 0) return launch_gm_sv<BITS, ST, true>(A, gate_up, in, grid, lds, s);
-  return launch_gm_sv<BITS, ST, false>(A, gate_up, in, grid, lds, s);
+  const bool sv = A.m0.cols / 64 % 4 == 0;
+  if (nw == 8)
+    return sv ? launch_gm_nw<BITS, ST, true, 8>(A, gate_up, in, grid, lds, s)
+              : launch_gm_nw<BITS, ST, false, 8>(A, gate_up, in, grid, lds, s);
+  return sv ? launch_gm_nw<BITS, ST, true, 4>(A, gate_up, in, grid, lds, s)
+            : launch_gm_nw<BITS, ST, false, 4>(A, gate_up, in, grid, lds, s);
 }
 
 }  // namespace smoe

@@ -38,15 +38,16 @@ __host__ __device__ inline GvLds gv_lds_layout(int cols, int lpr, int nk, int tc
   return L;
 }
 
-// LDS layout of the matrix-core stage (32-bit words): token pairs [TC * cols
-// / 2] (+ the same again for the lo halves of split inputs), K [G][16],
-// output scales [16], per-wave statistics [TC][GV_WAVES][2], and the k-split
-// partial sums [GV_WAVES][64][8]. Every region starts 16-byte aligned.
+// LDS layout of the matrix-core stage (32-bit words) for a workgroup of nw
+// waves: token pairs [TC * cols / 2] (+ the same again for the lo halves of
+// split inputs), K [G][16], output scales [16], per-wave statistics
+// [TC][nw][2], and the k-split partial sums [nw][64][8]. Every region starts
+// 16-byte aligned.
 struct GmLds {
   int x, xlo, k, osc, red, part, total;
 };
 
-__host__ __device__ inline GmLds gm_lds_layout(int cols, int tc, bool split) {
+__host__ __device__ inline GmLds gm_lds_layout(int cols, int tc, bool split, int nw) {
   auto al4 = [](int n) { return (n + 3) & ~3; };
   GmLds L;
   L.x = 0;
@@ -54,8 +55,8 @@ __host__ __device__ inline GmLds gm_lds_layout(int cols, int tc, bool split) {
   L.k = L.xlo + (split ? al4(tc * cols / 2) : 0);
   L.osc = L.k + al4(cols / 64 * 16);
   L.red = L.osc + 16;
-  L.part = L.red + al4(tc * GV_WAVES * 2);
-  L.total = L.part + GV_WAVES * 64 * 8;
+  L.part = L.red + al4(tc * nw * 2);
+  L.total = L.part + nw * 64 * 8;
   return L;
 }
 
@@ -95,7 +96,7 @@ hipError_t launch_dn(const GemvArgs& A, dim3 grid, unsigned lds, hipStream_t s);
 // Matrix-core stage launchers (smoe_gemm.hpp, instantiated per (BITS, scale
 // type) by smoe_gemm_inst.hip); in: GvIn of the activations.
 template <int BITS, typename ST>
-hipError_t launch_gm(const GemvArgs& A, bool gate_up, int in, dim3 grid, unsigned lds,
+hipError_t launch_gm(const GemvArgs& A, bool gate_up, int in, int nw, dim3 grid, unsigned lds,
                      hipStream_t s);
 
 }  // namespace smoe

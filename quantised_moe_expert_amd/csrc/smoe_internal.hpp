@@ -55,6 +55,12 @@ enum XMode : int {
   X_F32_RMS = 2,    // fp32 residual stream; the stage applies unit-gain RMSNorm
 };
 
+// Grouping (T > 1) keeps a token bitmask per expert in LDS: E * ceil(T / 32)
+// words plus 2 E, at most 160 KB.
+inline bool group_fits(int E, int T) {
+  return (int64_t)E * ((T + 31) / 32) * 4 + (int64_t)E * 8 <= 160 * 1024;
+}
+
 hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int32_t* ids,
                         float* w, int32_t* user_ids, float* user_w, int group, int* meta,
                         int* active, int* offs, int* pair_token, int* pair_of,

@@ -265,6 +265,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int3
   if (!group) return hipGetLastError();
   const int TW = (T + 31) / 32;
   const size_t lds = (size_t)E * TW * 4 + (size_t)E * 8;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_group,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), lds, stream, A);
   return hipGetLastError();
 }
@@ -369,11 +374,13 @@ static void grouped_shape(const MatPlan& m, bool split, int slots, GemvArgs& A, 
 // Launch shape of a matrix-core stage: 16-row tiles, one per wave, or one
 // per workgroup with its groups split over the four waves when one tile per
 // wave leaves under 1024 workgroups. Tokens per chunk: twice the mean pairs
-// per slot (at least 8, at most 16, one MFMA's M) so that the LDS a
-// workgroup holds stays small enough for several workgroups per CU, then cut
-// to fit 64 KB; slots with more pairs take several chunks. The k-split
-// partial-sum region (last in the layout) is allocated only when used.
-// False when not even one token fits.
+// per slot (at least 8, at most 16, one MFMA's M), cut to what the LDS
+// holds; slots with more pairs take several chunks, each of which reads the
+// weights again. Four-wave workgroups keep their LDS within 64 KB (two per
+// CU); when that would cut a full 16-token chunk short (large batches, long
+// rows) the workgroup has eight waves and up to 160 KB, one per CU, so the
+// weights are read fewer times. The k-split partial-sum region (last in the
+// layout) is allocated only when used. False when not even one token fits.
 #ifndef SMOE_GM_TPW_MAX
 #define SMOE_GM_TPW_MAX 4
 #endif
@@ -381,11 +388,19 @@ static void grouped_shape(const MatPlan& m, bool split, int slots, GemvArgs& A, 
 #define SMOE_GM_TC_MIN 8
 #endif
 static bool gm_shape(const MatPlan& m, bool split, int pairs, int slots, GemvArgs& A, dim3& grid,
-                     unsigned& lds) {
+                     unsigned& lds, int& nw) {
   const int tiles = (m.rows + 15) / 16;
-  const int ks = (int64_t)(tiles + GV_WAVES - 1) / GV_WAVES * slots < 1024 ? GV_WAVES : 1;
+  const int mean = (pairs + slots - 1) / slots;
+  const int want = 2 * mean < SMOE_GM_TC_MIN ? SMOE_GM_TC_MIN : (2 * mean > 16 ? 16 : 2 * mean);
+  auto bytes = [&](int t, int w, int k) {
+    const GmLds L = gm_lds_layout(m.cols, t, split, w);
+    return (k > 1 ? L.total : L.part) * 4;
+  };
+  nw = 4;
+  if (mean >= 16 && bytes(want, 4, 1) > 65536 && bytes(want, 8, 1) <= 160 * 1024) nw = 8;
+  const int ks = nw == 4 && (int64_t)(tiles + nw - 1) / nw * slots < 1024 ? nw : 1;
   A.ksplit = ks;
-  const int tpb = GV_WAVES / ks;
+  const int tpb = nw / ks;
   // tiles per wave: more while the grid keeps over 1024 workgroups, so that
   // each staging of the tokens serves more rows
   int tpw = 1;
@@ -395,24 +410,20 @@ static bool gm_shape(const MatPlan& m, bool split, int pairs, int slots, GemvArg
       tpw *= 2;
   A.tiles_per_wave = tpw;
   grid = dim3((tiles + tpb * tpw - 1) / (tpb * tpw), slots);
-  const int mean = (pairs + slots - 1) / slots;
-  int tc = 2 * mean < SMOE_GM_TC_MIN ? SMOE_GM_TC_MIN : (2 * mean > 16 ? 16 : 2 * mean);
-  auto bytes = [&](int t) {
-    const GmLds L = gm_lds_layout(m.cols, t, split);
-    return (ks > 1 ? L.total : L.part) * 4;
-  };
-  while (tc > 0 && bytes(tc) > 65536) --tc;
+  const int cap = nw == 8 ? 160 * 1024 : 65536;
+  int tc = want;
+  while (tc > 0 && bytes(tc, nw, ks) > cap) --tc;
   if (tc == 0) return false;
   A.tc = tc;
-  lds = (unsigned)bytes(tc);
+  lds = (unsigned)bytes(tc, nw, ks);
   return true;
 }
 
 template <typename ST>
-static hipError_t gm_dispatch(int bits, const GemvArgs& A, bool gate_up, int in, dim3 grid,
-                              unsigned lds, hipStream_t s) {
-  return bits == 4 ? launch_gm<4, ST>(A, gate_up, in, grid, lds, s)
-                   : launch_gm<2, ST>(A, gate_up, in, grid, lds, s);
+static hipError_t gm_dispatch(int bits, const GemvArgs& A, bool gate_up, int in, int nw,
+                              dim3 grid, unsigned lds, hipStream_t s) {
+  return bits == 4 ? launch_gm<4, ST>(A, gate_up, in, nw, grid, lds, s)
+                   : launch_gm<2, ST>(A, gate_up, in, nw, grid, lds, s);
 }
 
 hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xmode,
@@ -439,11 +450,11 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
   const int in = xmode == X_BF16 ? GV_BF16 : GV_F32_SPLIT;
   dim3 grid;
   unsigned lds;
-  if (gm_shape(P.gate, in == GV_F32_SPLIT, pairs, shared ? 1 : max_slots, A,
-               grid, lds))
+  int nw;
+  if (gm_shape(P.gate, in == GV_F32_SPLIT, pairs, shared ? 1 : max_slots, A, grid, lds, nw))
     return L.desc.scale_dtype == SMOE_SCALE_F32
-               ? gm_dispatch<float>(L.desc.bits, A, true, in, grid, lds, stream)
-               : gm_dispatch<_Float16>(L.desc.bits, A, true, in, grid, lds, stream);
+               ? gm_dispatch<float>(L.desc.bits, A, true, in, nw, grid, lds, stream)
+               : gm_dispatch<_Float16>(L.desc.bits, A, true, in, nw, grid, lds, stream);
   grouped_shape(P.gate, in == GV_F32_SPLIT, shared ? 1 : max_slots, A, grid, lds);
   const int v = P.gate.v;
   if (L.desc.bits == 4)
@@ -475,10 +486,11 @@ hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, i
   A.out = y;
   dim3 grid;
   unsigned lds;
-  if (gm_shape(P.down, false, pairs, shared ? 1 : max_slots, A, grid, lds))
+  int nw;
+  if (gm_shape(P.down, false, pairs, shared ? 1 : max_slots, A, grid, lds, nw))
     return L.desc.scale_dtype == SMOE_SCALE_F32
-               ? gm_dispatch<float>(L.desc.bits, A, false, GV_F32, grid, lds, stream)
-               : gm_dispatch<_Float16>(L.desc.bits, A, false, GV_F32, grid, lds, stream);
+               ? gm_dispatch<float>(L.desc.bits, A, false, GV_F32, nw, grid, lds, stream)
+               : gm_dispatch<_Float16>(L.desc.bits, A, false, GV_F32, nw, grid, lds, stream);
   grouped_shape(P.down, false, shared ? 1 : max_slots, A, grid, lds);
   const int v = P.down.v;
   if (L.desc.bits == 4)

@@ -73,6 +73,11 @@ WORKLOADS = {
     # DeepSeek-MoE-16B-shaped layer, 8 tokens, plus an always-on shared expert
     "deepseek16b_q4_b8": Workload("deepseek16b_q4_b8", 2048, 1408, 64, 6, 8, 4, False,
                                   shared_ffn_dim=2816, seed=4),
+    # the same layer at prefill-sized batches (matrix-core grouped stages)
+    "qwen235b_q4_t512": Workload("qwen235b_q4_t512", 4096, 1536, 128, 8, 512, 4, True,
+                                 seed=6),
+    "qwen235b_q4_t2048": Workload("qwen235b_q4_t2048", 4096, 1536, 128, 8, 2048, 4, True,
+                                  seed=7),
     # 94 stacked Qwen3-235B-shaped layers, batch 1, RMSNorm + residual per layer
     "qwen235b_q4_stack94": Workload("qwen235b_q4_stack94", 4096, 1536, 128, 8, 1, 4, True,
                                     n_layers=94, x_dtype="f32", seed=5),

@@ -76,8 +76,24 @@ def test_load_blobs_accepts_a_valid_bank_and_frees():
     assert smoe.smoe_workspace_bytes(h, 32, 8) > smoe.smoe_workspace_bytes(h, 1, 8)
     assert smoe.smoe_workspace_bytes(h, 1, 0) == 0
     assert smoe.smoe_workspace_bytes(h, smoe.SMOE_MAX_TOKENS + 1, 8) == 0
+    assert smoe.smoe_workspace_bytes(h, smoe.SMOE_MAX_TOKENS, 8) > 0
     smoe.smoe_free(h)
     smoe.smoe_free(None)
+
+
+def test_grouping_that_does_not_fit_lds_is_unsupported():
+    # 512 experts x 4096 tokens: 256 KB of token bitmasks (the limit is 160 KB)
+    desc = _desc(num_experts=512)
+    h = smoe.smoe_load_blobs(desc, FAKE, 512 * desc.blob_stride)
+    try:
+        assert smoe.smoe_workspace_bytes(h, 4096, 8) == 0
+        assert smoe.smoe_workspace_bytes(h, 2048, 8) > 0
+        with pytest.raises(smoe.SmoeError) as e:
+            smoe.smoe_moe_forward(h, FAKE, smoe.SMOE_DTYPE_BF16, FAKE, 4096, 8, True, FAKE, 0, 0,
+                                  FAKE, 1 << 40, 0)
+        assert e.value.code == smoe.SMOE_E_UNSUPPORTED
+    finally:
+        smoe.smoe_free(h)
 
 
 @pytest.mark.parametrize("kw,nbytes_delta,ptr,code", [

@@ -282,6 +282,42 @@ def test_qwen235b_b32_sampled(name):
     _check_layer(hl, x, lg, W.top_k, W.norm_topk_prob, "bf16", tokens=[0, 13, 31])
 
 
+# Prefill-sized batches: 32 pairs per expert fill whole 16-token chunks; with
+# d = 2304 a 16-token chunk needs more than 64 KB of LDS, so the gate/up
+# stage runs in eight-wave workgroups.
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_prefill_sized_batch_eight_wave_chunks(x_dtype):
+    _torch()
+    hl = random_layer(4242, 2304, 256, 8, 4, "f32")
+    r = synth.rng(4243)
+    T = 128
+    x = _x(r, T, 2304, x_dtype)
+    lg = synth.normal_f32(r, (T, 8))
+    _check_layer(hl, x, lg, 2, True, x_dtype)
+
+
+def test_qwen235b_q4_t512_sampled():
+    _torch()
+    W = synth.WORKLOADS["qwen235b_q4_t512"]
+    hl = random_layer(W.seed, W.d_model, W.ffn_dim, W.num_experts, W.bits)
+    r = synth.rng(W.seed + 4000)
+    x = _x(r, W.n_tokens, W.d_model, "bf16")
+    lg = synth.normal_f32(r, (W.n_tokens, W.num_experts))
+    _check_layer(hl, x, lg, W.top_k, W.norm_topk_prob, "bf16", tokens=[0, 257, 511])
+
+
+def test_max_tokens_grouping_beyond_64k_lds():
+    # 4096 tokens over 128 experts: the grouping's token bitmasks take 65.5 KB
+    _torch()
+    import quantised_moe_expert_amd as smoe
+    T = smoe.SMOE_MAX_TOKENS
+    hl = random_layer(77, 256, 128, 128, 4, "f16")
+    r = synth.rng(78)
+    x = _x(r, T, 256, "bf16")
+    lg = synth.normal_f32(r, (T, 128))
+    _check_layer(hl, x, lg, 8, True, "bf16", tokens=[0, 1, 2047, T - 1])
+
+
 def test_deepseek16b_q4_b8_full():
     _torch()
     W = synth.WORKLOADS["deepseek16b_q4_b8"]
