@@ -60,6 +60,7 @@ __all__ = [
     "TensorSpan", "ExpertLayout", "expert_layout",
     "build_expert_blob", "read_expert_tensors",
     "OracleLayer", "route", "softmax64", "silu", "swiglu_expert",
+    "RouteOpts", "route_ex", "sigmoid32",
     "moe_forward", "rms_norm", "decode_step",
 ]
 
@@ -357,6 +358,87 @@ def route(logits_row: np.ndarray, top_k: int, norm_topk_prob: bool
     return ids, w
 
 
+class RouteOpts:
+    """Routing variants ("CMF v2 Format Specification", 2.2 MoE; 5. Masks
+    section). Defaults reproduce plain softmax routing.
+
+    sigmoid        score each expert with sigmoid(logit) instead of the
+                   softmax over all logits.
+    expert_bias    [E] added to the scores for the top-k selection only; the
+                   weights are the unbiased scores.
+    scaling        routed_scaling_factor, applied to the routed weights after
+                   the optional renormalisation.
+    mask           [E] bools, the routable experts: selection runs over them
+                   only and the softmax is taken over them only (other
+                   experts get no probability mass); None = all routable.
+    shared_gate    [T] fp32 logits; the shared expert's output is weighted by
+                   sigmoid(shared_gate[t]) instead of 1."""
+
+    def __init__(self, sigmoid: bool = False, expert_bias=None, scaling: float = 1.0,
+                 mask=None, shared_gate=None):
+        self.sigmoid = bool(sigmoid)
+        self.expert_bias = None if expert_bias is None else np.asarray(expert_bias, np.float32)
+        self.scaling = float(np.float32(scaling))
+        self.mask = None if mask is None else np.asarray(mask, dtype=bool)
+        self.shared_gate = None if shared_gate is None else np.asarray(shared_gate, np.float32)
+
+    def is_default(self) -> bool:
+        return (not self.sigmoid and self.expert_bias is None and self.scaling == 1.0
+                and self.mask is None and self.shared_gate is None)
+
+
+def sigmoid32(l32: np.ndarray) -> np.ndarray:
+    """sigmoid in float32 arithmetic: 1 / (1 + exp(-x))."""
+    l32 = np.asarray(l32, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        return (np.float32(1.0) / (np.float32(1.0) + np.exp(-l32))).astype(np.float32)
+
+
+def route_ex(logits_row: np.ndarray, top_k: int, norm_topk_prob: bool,
+             opts: "RouteOpts") -> Tuple[List[int], np.ndarray]:
+    """Top-k routing with the variants of RouteOpts, in the order the format
+    states: score (softmax over the routable experts, or sigmoid per expert),
+    select the top-k by score + bias (ties to the lower id), gather the
+    unbiased scores, renormalise if asked, then multiply by the scaling
+    factor.
+
+    Without a bias the selection compares the fp32 logits (the scores are
+    monotone in them); with a bias it compares fp32 score + bias, the score
+    computed in fp32 (1/(1+exp(-x)), or exp(x - max)/sum over the routable
+    experts), which is the precision the kernels decide in. Weights are fp64
+    except the fp32 scores that selection used."""
+    l32 = np.asarray(logits_row, dtype=np.float32).reshape(-1)
+    E = l32.size
+    mask = np.ones(E, dtype=bool) if opts.mask is None else opts.mask.reshape(-1)
+    if mask.size != E:
+        raise ValueError("mask needs one entry per expert")
+    routable = [e for e in range(E) if mask[e]]
+    if not (1 <= top_k <= min(MAX_TOP_K, len(routable))):
+        raise ValueError(f"top_k must be in [1, min(16, routable experts)], got {top_k}")
+    if opts.expert_bias is None:
+        keyv = [float(v) for v in l32]
+    else:
+        if opts.sigmoid:
+            sc32 = sigmoid32(l32)
+        else:
+            lr = l32[mask]
+            ex = np.exp((l32 - np.max(lr)).astype(np.float32)).astype(np.float32)
+            den = np.float32(np.sum(ex[mask], dtype=np.float32))
+            sc32 = (ex / den).astype(np.float32)
+        b32 = opts.expert_bias.reshape(-1).astype(np.float32)
+        keyv = [float(np.float32(sc32[e] + b32[e])) for e in range(E)]
+    ids = sorted(routable, key=lambda e: (-keyv[e], e))[:top_k]
+    if opts.sigmoid:
+        p = 1.0 / (1.0 + np.exp(-l32.astype(np.float64)))
+    else:
+        p = np.zeros(E, dtype=np.float64)
+        p[mask] = softmax64(l32[mask])
+    w = np.array([p[e] for e in ids], dtype=np.float64)
+    if norm_topk_prob:
+        w = w / np.sum(w)
+    return ids, w * opts.scaling
+
+
 # --------------------------------------------------------------------------
 # Expert FFN (SwiGLU) and the layer
 # --------------------------------------------------------------------------
@@ -420,12 +502,14 @@ class OracleLayer:
 
 def moe_forward(layer: OracleLayer, x: np.ndarray, logits: np.ndarray,
                 top_k: int, norm_topk_prob: bool,
-                tokens: Optional[Sequence[int]] = None
+                tokens: Optional[Sequence[int]] = None,
+                opts: Optional["RouteOpts"] = None
                 ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """out[t] = sum_j w[t,j] * FFN_{ids[t,j]}(x[t]) (+ shared FFN(x[t]) with
-    weight 1). x is [T, d] (any float dtype, taken exactly), logits [T, E]
-    fp32. Returns (out float64 [T', d], ids int [T', k], w float64 [T', k])
-    for the requested tokens (all by default)."""
+    weight 1, or sigmoid(opts.shared_gate[t])). x is [T, d] (any float dtype,
+    taken exactly), logits [T, E] fp32. Routing is route(), or route_ex()
+    with opts. Returns (out float64 [T', d], ids int [T', k], w float64
+    [T', k]) for the requested tokens (all by default)."""
     x = np.asarray(x, dtype=np.float64)
     logits = np.asarray(logits, dtype=np.float32)
     T = x.shape[0]
@@ -435,14 +519,20 @@ def moe_forward(layer: OracleLayer, x: np.ndarray, logits: np.ndarray,
     w_all = np.zeros((len(toks), top_k), dtype=np.float64)
     sh = layer.shared_weights()
     for i, t in enumerate(toks):
-        ids, w = route(logits[t], top_k, norm_topk_prob)
+        if opts is None:
+            ids, w = route(logits[t], top_k, norm_topk_prob)
+        else:
+            ids, w = route_ex(logits[t], top_k, norm_topk_prob, opts)
         ids_all[i] = ids
         w_all[i] = w
         for j, e in enumerate(ids):
             W = layer.expert_weights(e)
             out[i] += w[j] * swiglu_expert(W["gate"], W["up"], W["down"], x[t])
         if sh is not None:
-            out[i] += swiglu_expert(sh["gate"], sh["up"], sh["down"], x[t])
+            ws = 1.0
+            if opts is not None and opts.shared_gate is not None:
+                ws = 1.0 / (1.0 + np.exp(-np.float64(opts.shared_gate.reshape(-1)[t])))
+            out[i] += ws * swiglu_expert(sh["gate"], sh["up"], sh["down"], x[t])
     return out, ids_all, w_all
 
 
