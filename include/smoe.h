@@ -162,6 +162,47 @@ uint64_t smoe_workspace_bytes(const smoe_layer* layer, int n_tokens, int top_k);
 int smoe_route(const float* d_logits, int n_tokens, int n_experts, int top_k,
                int norm_topk_prob, int32_t* d_ids, float* d_weights, void* hip_stream);
 
+/* Routing variants ("CMF v2 Format Specification", 2.2 MoE; 5. Masks
+ * section). smoe_route_opts_init() sets the defaults (plain softmax routing,
+ * no bias, factor 1, every expert routable, shared expert weight 1).
+ *  sigmoid           0: softmax over the routable experts' logits; 1: each
+ *                    expert scored by sigmoid(logit) on its own.
+ *  scaling_factor    routed_scaling_factor: multiplies the routed weights
+ *                    after the optional renormalisation; finite.
+ *  d_expert_bias     device [num_experts] fp32, nullable: added to the
+ *                    scores for the top-k selection only (the weights stay
+ *                    the unbiased scores). With a bias the selection
+ *                    compares fp32 score + bias; without one it compares
+ *                    the logits (the same order).
+ *  d_shared_gate     device [n_tokens] fp32, nullable: per-token logits of
+ *                    the shared-expert gate; the shared expert's output is
+ *                    weighted by sigmoid(logit) instead of 1.
+ *  use_mask, expert_mask
+ *                    host bitfield of routable experts, bit e of word e / 32
+ *                    (LSB-first, the masks section's byte order read as
+ *                    little-endian words): selection runs over set bits
+ *                    only and the softmax is taken over them only. Bits at
+ *                    or past num_experts must be 0 and at least top_k bits
+ *                    must be set (SMOE_E_ARG otherwise). Copied at the call.
+ * Variant routing always takes the grouped (batch) kernels, also for one
+ * token. */
+typedef struct smoe_route_opts {
+  int32_t sigmoid;
+  float scaling_factor;
+  const float* d_expert_bias;
+  const float* d_shared_gate;
+  int32_t use_mask;
+  uint32_t expert_mask[SMOE_MAX_EXPERTS / 32];
+} smoe_route_opts;
+
+void smoe_route_opts_init(smoe_route_opts* opts);
+
+/* smoe_route with routing variants (opts nullable = defaults). Errors as
+ * smoe_route, plus SMOE_E_ARG for an invalid mask or a non-finite factor. */
+int smoe_route_ex(const float* d_logits, int n_tokens, int n_experts, int top_k,
+                  int norm_topk_prob, const smoe_route_opts* opts, int32_t* d_ids,
+                  float* d_weights, void* hip_stream);
+
 /* One MoE layer forward:
  *   out[t] = sum_j w[t,j] * down_e(silu(gate_e x[t]) * up_e x[t])   (e = ids[t,j])
  *            + shared(x[t])                                         (if present)
@@ -184,6 +225,16 @@ int smoe_moe_forward(const smoe_layer* layer, const void* d_x, int x_dtype,
                      const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
                      float* d_out, int32_t* d_topk_ids, float* d_topk_w,
                      void* d_workspace, uint64_t ws_bytes, void* hip_stream);
+
+/* smoe_moe_forward with routing variants (opts nullable = defaults); d_out
+ * gets sum_j w_j FFN_j(x) + sigmoid(shared_gate) * FFN_shared(x), d_topk_w the
+ * final weights (renormalised and scaled). Errors as smoe_moe_forward and
+ * smoe_route_ex. */
+int smoe_moe_forward_ex(const smoe_layer* layer, const void* d_x, int x_dtype,
+                        const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
+                        const smoe_route_opts* opts, float* d_out, int32_t* d_topk_ids,
+                        float* d_topk_w, void* d_workspace, uint64_t ws_bytes,
+                        void* hip_stream);
 
 /* Stacked decode step over n_layers MoE layers (same d_model):
  *   for l in 0..n_layers-1:  h = h + MoE_l(rms_norm(h, eps))

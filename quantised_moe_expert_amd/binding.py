@@ -42,7 +42,8 @@ SMOE_KERNEL_DOWN = 2
 EXPORTED = (
     "smoe_version", "smoe_last_error", "smoe_expert_layout_of", "smoe_load_blobs",
     "smoe_free", "smoe_workspace_bytes", "smoe_route", "smoe_moe_forward",
-    "smoe_decode_step", "smoe_trace_kernel",
+    "smoe_decode_step", "smoe_trace_kernel", "smoe_route_opts_init", "smoe_route_ex",
+    "smoe_moe_forward_ex",
 )
 
 
@@ -50,6 +51,37 @@ class SmoeError(RuntimeError):
     def __init__(self, code: int, message: str):
         super().__init__(f"smoe error {code}: {message}")
         self.code = code
+
+
+class smoe_route_opts(ctypes.Structure):
+    """Routing variants (see smoe_route_opts in include/smoe.h)."""
+    _fields_ = [
+        ("sigmoid", ctypes.c_int32),
+        ("scaling_factor", ctypes.c_float),
+        ("d_expert_bias", ctypes.c_void_p),
+        ("d_shared_gate", ctypes.c_void_p),
+        ("use_mask", ctypes.c_int32),
+        ("expert_mask", ctypes.c_uint32 * (SMOE_MAX_EXPERTS // 32)),
+    ]
+
+
+def make_route_opts(sigmoid: bool = False, scaling_factor: float = 1.0, d_expert_bias: int = 0,
+                    d_shared_gate: int = 0, routable: Optional[Sequence[bool]] = None
+                    ) -> smoe_route_opts:
+    """smoe_route_opts from Python values; routable: one bool per expert (None =
+    all), packed LSB-first into the mask words."""
+    o = smoe_route_opts()
+    load_library().smoe_route_opts_init(ctypes.byref(o))
+    o.sigmoid = int(bool(sigmoid))
+    o.scaling_factor = float(scaling_factor)
+    o.d_expert_bias = d_expert_bias or None
+    o.d_shared_gate = d_shared_gate or None
+    if routable is not None:
+        o.use_mask = 1
+        for e, on in enumerate(routable):
+            if on:
+                o.expert_mask[e // 32] |= 1 << (e % 32)
+    return o
 
 
 class smoe_layer_desc(ctypes.Structure):
@@ -129,6 +161,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                      ctypes.c_float, _P, _U64, _P]
     lib.smoe_trace_kernel.restype = _I
     lib.smoe_trace_kernel.argtypes = [_I, _P, _P]
+    lib.smoe_route_opts_init.restype = None
+    lib.smoe_route_opts_init.argtypes = [ctypes.POINTER(smoe_route_opts)]
+    lib.smoe_route_ex.restype = _I
+    lib.smoe_route_ex.argtypes = [_P, _I, _I, _I, _I, ctypes.POINTER(smoe_route_opts), _P, _P,
+                                  _P]
+    lib.smoe_moe_forward_ex.restype = _I
+    lib.smoe_moe_forward_ex.argtypes = [_P, _P, _I, _P, _I, _I, _I,
+                                        ctypes.POINTER(smoe_route_opts), _P, _P, _P, _P, _U64,
+                                        _P]
     if path is None:
         _lib = lib
     return lib
@@ -195,6 +236,26 @@ def smoe_moe_forward(layer: int, d_x: int, x_dtype: int, d_logits: int, n_tokens
         layer, d_x or None, x_dtype, d_logits or None, n_tokens, top_k,
         int(bool(norm_topk_prob)), d_out or None, d_topk_ids or None, d_topk_w or None,
         d_workspace or None, ws_bytes, hip_stream or None))
+
+
+def smoe_route_ex(d_logits: int, n_tokens: int, n_experts: int, top_k: int,
+                  norm_topk_prob: bool, opts: Optional[smoe_route_opts], d_ids: int,
+                  d_weights: int, hip_stream: int = 0) -> None:
+    _check(load_library().smoe_route_ex(d_logits or None, n_tokens, n_experts, top_k,
+                                        int(bool(norm_topk_prob)),
+                                        ctypes.byref(opts) if opts is not None else None,
+                                        d_ids or None, d_weights or None, hip_stream or None))
+
+
+def smoe_moe_forward_ex(layer: int, d_x: int, x_dtype: int, d_logits: int, n_tokens: int,
+                        top_k: int, norm_topk_prob: bool, opts: Optional[smoe_route_opts],
+                        d_out: int, d_topk_ids: int, d_topk_w: int, d_workspace: int,
+                        ws_bytes: int, hip_stream: int = 0) -> None:
+    _check(load_library().smoe_moe_forward_ex(
+        layer, d_x or None, x_dtype, d_logits or None, n_tokens, top_k,
+        int(bool(norm_topk_prob)), ctypes.byref(opts) if opts is not None else None,
+        d_out or None, d_topk_ids or None, d_topk_w or None, d_workspace or None, ws_bytes,
+        hip_stream or None))
 
 
 def smoe_decode_step(layers: Sequence[int], d_h: int, d_logits: int, n_tokens: int,

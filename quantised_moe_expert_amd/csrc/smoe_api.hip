@@ -10,6 +10,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <cmath>
+#include <cstring>
 #include <mutex>
 #include <new>
 
@@ -137,7 +139,7 @@ int check_hip(hipError_t e, const char* what) {
 // residual stream with RMSNorm applied on the way in).
 int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const float* logits,
                  int T, int k, int norm, float* out, int accumulate, int32_t* uids, float* uw,
-                 uint8_t* ws, hipStream_t s) {
+                 uint8_t* ws, hipStream_t s, const RouteCfg& cfg = RouteCfg()) {
   const WsLayout W = ws_layout(L, T, k);
   int32_t* ids = (int32_t*)(ws + W.ids);
   float* w = (float*)(ws + W.w);
@@ -151,7 +153,7 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
   const int E = (int)L.desc.num_experts;
   const int max_slots = T * k < E ? T * k : E;
   int rc;
-  if (T == 1 && !g_force_multi) {
+  if (T == 1 && !g_force_multi && cfg.is_default()) {
     bool launched = false;
     if ((rc = check_hip(decode1_try(L, x, xmode != X_BF16, xmode == X_F32_RMS, eps, logits, k,
                                     norm, out, accumulate, uids, uw, h, ids, w, s, &launched),
@@ -160,7 +162,7 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
     if (launched) return SMOE_OK;
   }
   if ((rc = check_hip(launch_route(logits, T, E, k, norm, ids, w, uids, uw, 1, meta, active,
-                                   offs, pair_token, pair_of, s),
+                                   offs, pair_token, pair_of, s, cfg),
                       "route launch")))
     return rc;
   {
@@ -189,7 +191,8 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
   }
   if (rc) return rc;
   return check_hip(
-      launch_combine(y, pair_of, w, ysh, out, T, k, (int)L.desc.d_model, accumulate, s),
+      launch_combine(y, pair_of, w, ysh, cfg.shared_gate, out, T, k, (int)L.desc.d_model,
+                     accumulate, s),
       "combine launch");
 }
 
@@ -283,20 +286,72 @@ uint64_t smoe_workspace_bytes(const smoe_layer* layer, int n_tokens, int top_k) 
   return ws_layout(layer->info, n_tokens, top_k).total;
 }
 
+// Validates opts against E and k and turns them into the kernels' form.
+static int route_cfg(const smoe_route_opts* opts, int n_experts, int top_k, RouteCfg* cfg) {
+  *cfg = RouteCfg();
+  if (!opts) return SMOE_OK;
+  if (opts->sigmoid != 0 && opts->sigmoid != 1) return fail(SMOE_E_ARG, "sigmoid must be 0 or 1");
+  if (!std::isfinite(opts->scaling_factor))
+    return fail(SMOE_E_ARG, "scaling_factor must be finite");
+  if (opts->d_expert_bias && !aligned(opts->d_expert_bias, 4))
+    return fail(SMOE_E_ARG, "expert bias must be 4-byte aligned");
+  if (opts->d_shared_gate && !aligned(opts->d_shared_gate, 4))
+    return fail(SMOE_E_ARG, "shared gate must be 4-byte aligned");
+  cfg->sigmoid = opts->sigmoid;
+  cfg->scale = opts->scaling_factor;
+  cfg->bias = opts->d_expert_bias;
+  cfg->shared_gate = opts->d_shared_gate;
+  if (opts->use_mask) {
+    int routable = 0;
+    for (int wd = 0; wd < SMOE_MAX_EXPERTS / 32; ++wd) {
+      uint32_t m = opts->expert_mask[wd];
+      for (int b = 0; b < 32; ++b)
+        if ((m >> b) & 1u) {
+          if (wd * 32 + b >= n_experts)
+            return fail(SMOE_E_ARG, "expert mask bit %d set past num_experts %d", wd * 32 + b,
+                        n_experts);
+          ++routable;
+        }
+      cfg->mask[wd] = m;
+    }
+    if (routable < top_k)
+      return fail(SMOE_E_ARG, "expert mask leaves %d routable experts for top_k %d", routable,
+                  top_k);
+    cfg->use_mask = 1;
+  }
+  return SMOE_OK;
+}
+
+void smoe_route_opts_init(smoe_route_opts* opts) {
+  if (!opts) return;
+  std::memset(opts, 0, sizeof(*opts));
+  opts->scaling_factor = 1.0f;
+}
+
 int smoe_route(const float* d_logits, int n_tokens, int n_experts, int top_k,
                int norm_topk_prob, int32_t* d_ids, float* d_weights, void* hip_stream) {
+  return smoe_route_ex(d_logits, n_tokens, n_experts, top_k, norm_topk_prob, nullptr, d_ids,
+                       d_weights, hip_stream);
+}
+
+int smoe_route_ex(const float* d_logits, int n_tokens, int n_experts, int top_k,
+                  int norm_topk_prob, const smoe_route_opts* opts, int32_t* d_ids,
+                  float* d_weights, void* hip_stream) {
   if (n_tokens < 0 || n_tokens > SMOE_MAX_TOKENS)
     return fail(SMOE_E_ARG, "n_tokens must be in [0, %d]", SMOE_MAX_TOKENS);
   if (n_experts < 1 || n_experts > SMOE_MAX_EXPERTS)
     return fail(SMOE_E_ARG, "n_experts must be in [1, %d]", SMOE_MAX_EXPERTS);
   const int kmax = n_experts < SMOE_MAX_TOP_K ? n_experts : SMOE_MAX_TOP_K;
   if (top_k < 1 || top_k > kmax) return fail(SMOE_E_ARG, "top_k must be in [1, %d]", kmax);
+  RouteCfg cfg;
+  int rc = route_cfg(opts, n_experts, top_k, &cfg);
+  if (rc) return rc;
   if (n_tokens == 0) return ok();
   if (!d_logits || !d_ids || !d_weights) return fail(SMOE_E_ARG, "null pointer argument");
-  int rc = check_hip(launch_route(d_logits, n_tokens, n_experts, top_k, norm_topk_prob != 0,
-                                  d_ids, d_weights, nullptr, nullptr, 0, nullptr, nullptr,
-                                  nullptr, nullptr, nullptr, (hipStream_t)hip_stream),
-                     "route launch");
+  rc = check_hip(launch_route(d_logits, n_tokens, n_experts, top_k, norm_topk_prob != 0, d_ids,
+                              d_weights, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr,
+                              nullptr, (hipStream_t)hip_stream, cfg),
+                 "route launch");
   return rc ? rc : ok();
 }
 
@@ -325,8 +380,20 @@ int smoe_moe_forward(const smoe_layer* layer, const void* d_x, int x_dtype,
                      const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
                      float* d_out, int32_t* d_topk_ids, float* d_topk_w, void* d_workspace,
                      uint64_t ws_bytes, void* hip_stream) {
+  return smoe_moe_forward_ex(layer, d_x, x_dtype, d_logits, n_tokens, top_k, norm_topk_prob,
+                             nullptr, d_out, d_topk_ids, d_topk_w, d_workspace, ws_bytes,
+                             hip_stream);
+}
+
+int smoe_moe_forward_ex(const smoe_layer* layer, const void* d_x, int x_dtype,
+                        const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
+                        const smoe_route_opts* opts, float* d_out, int32_t* d_topk_ids,
+                        float* d_topk_w, void* d_workspace, uint64_t ws_bytes,
+                        void* hip_stream) {
   int rc = check_forward_args(layer, n_tokens, top_k, d_workspace, ws_bytes);
   if (rc) return rc;
+  RouteCfg cfg;
+  if ((rc = route_cfg(opts, (int)layer->info.desc.num_experts, top_k, &cfg))) return rc;
   if (x_dtype != SMOE_DTYPE_BF16 && x_dtype != SMOE_DTYPE_F32)
     return fail(SMOE_E_ARG, "x_dtype must be SMOE_DTYPE_BF16 or SMOE_DTYPE_F32");
   if (n_tokens == 0) return ok();
@@ -336,7 +403,7 @@ int smoe_moe_forward(const smoe_layer* layer, const void* d_x, int x_dtype,
     return fail(SMOE_E_ARG, "logits and out must be 4-byte aligned");
   rc = forward_impl(layer->info, d_x, x_dtype == SMOE_DTYPE_BF16 ? X_BF16 : X_F32, 0.f,
                     d_logits, n_tokens, top_k, norm_topk_prob != 0, d_out, 0, d_topk_ids,
-                    d_topk_w, (uint8_t*)d_workspace, (hipStream_t)hip_stream);
+                    d_topk_w, (uint8_t*)d_workspace, (hipStream_t)hip_stream, cfg);
   return rc ? rc : ok();
 }
 

@@ -61,10 +61,24 @@ inline bool group_fits(int E, int T) {
   return (int64_t)E * ((T + 31) / 32) * 4 + (int64_t)E * 8 <= 160 * 1024;
 }
 
+// Routing variants, as the kernels take them (the ABI's smoe_route_opts
+// after validation). Default-constructed = plain softmax routing.
+struct RouteCfg {
+  int sigmoid = 0;
+  float scale = 1.0f;
+  const float* bias = nullptr;
+  const float* shared_gate = nullptr;
+  int use_mask = 0;
+  uint32_t mask[SMOE_MAX_EXPERTS / 32] = {};
+  bool is_default() const {
+    return !sigmoid && scale == 1.0f && !bias && !shared_gate && !use_mask;
+  }
+};
+
 hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int32_t* ids,
                         float* w, int32_t* user_ids, float* user_w, int group, int* meta,
                         int* active, int* offs, int* pair_token, int* pair_of,
-                        hipStream_t stream);
+                        hipStream_t stream, const RouteCfg& cfg = RouteCfg());
 
 // pairs: routed (token, expert) pairs of the call (T for the shared expert),
 // used to size the launch.
@@ -85,8 +99,10 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
                        int32_t* uids, float* uw, float* h, int32_t* ws_ids, float* ws_w,
                        hipStream_t stream, bool* launched);
 
+// shared_gate (nullable, [T] logits): the shared expert's weight is
+// sigmoid(shared_gate[t]) instead of 1.
 hipError_t launch_combine(const float* y, const int* pair_of, const float* w,
-                          const float* y_shared, float* out, int T, int k, int d,
-                          int accumulate, hipStream_t stream);
+                          const float* y_shared, const float* shared_gate, float* out, int T,
+                          int k, int d, int accumulate, hipStream_t stream);
 
 }  // namespace smoe

@@ -22,6 +22,7 @@ static_assert(SMOE_MAX_EXPERTS <= 512, "top-k kernels hold at most 8 logits per 
 struct RouteArgs {
   const float* logits;
   int T, E, k, norm, group;
+  RouteCfg cfg;
   int32_t* ids;
   float* w;
   int32_t* user_ids;
@@ -109,6 +110,11 @@ __device__ __forceinline__ float rt_wave_sum(float v) {
 // EPL = logits per lane (E <= 64 * EPL).
 constexpr int TOPK_THREADS = 256;
 
+// v from lane src (src wave-uniform)
+__device__ __forceinline__ float rt_lane_value(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+
 template <int EPL>
 __global__ __launch_bounds__(TOPK_THREADS) void k_topk(RouteArgs A) {
   const int lane = threadIdx.x & 63;
@@ -122,24 +128,45 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(RouteArgs A) {
     float lv[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) lv[i] = lg[min(lane + 64 * i, A.E - 1)];
-    uint64_t key[EPL];
+    // routable: inside E and, with a mask, its bit set
+    bool ok[EPL];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      float x = e < A.E ? lv[i] : -INFINITY;
-      if (x != x) x = -INFINITY;  // NaN never outranks a number
-      key[i] = e < A.E ? rt_key(x, e) : 0;
-      mx = fmaxf(mx, x);
+      ok[i] = e < A.E && (!A.cfg.use_mask || ((A.cfg.mask[e >> 5] >> (e & 31)) & 1u));
+      if (lv[i] != lv[i]) lv[i] = -INFINITY;  // NaN never outranks a number
+      if (ok[i]) mx = fmaxf(mx, lv[i]);
     }
-    mx = rt_wave_max(mx);
-    float se = 0.f;
+    // scores: sigmoid per expert, or the softmax over the routable experts
+    float sc[EPL];
+    if (A.cfg.sigmoid) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (key[i]) se += expf(rt_key_logit(key[i]) - mx);
-    se = rt_wave_sum(se);
-    // k rounds: the largest remaining key over the wave wins and its owner
-    // drops it
+      for (int i = 0; i < EPL; ++i) sc[i] = 1.0f / (1.0f + expf(-lv[i]));
+    } else {
+      mx = rt_wave_max(mx);
+      float se = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        sc[i] = expf(lv[i] - mx);
+        if (ok[i]) se += sc[i];
+      }
+      se = rt_wave_sum(se);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) sc[i] = sc[i] / se;
+    }
+    // selection keys (see rt_key; 0 = not routable): the logit, or with a
+    // bias the fp32 score + bias
+    uint64_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      const float b = A.cfg.bias ? A.cfg.bias[min(e, A.E - 1)] : 0.f;
+      const float kv = A.cfg.bias ? sc[i] + b : lv[i];
+      key[i] = ok[i] ? rt_key(kv, e) : 0;
+    }
+    // k rounds: the largest remaining key over the wave wins, its owner
+    // drops it and broadcasts the winner's score
     float wsum = 0.f;
     float wj[SMOE_MAX_TOP_K];
     int idj[SMOE_MAX_TOP_K];
@@ -150,12 +177,17 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(RouteArgs A) {
 #pragma unroll
         for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
         best = rt_wave_max_key(best);
+        const int id = rt_key_id(best);
+        float p = 0.f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
-          if (key[i] == best) key[i] = 0;
-        const float p = expf(rt_key_logit(best) - mx) / se;
+          if (key[i] == best) {
+            key[i] = 0;
+            p = sc[i];
+          }
+        p = rt_lane_value(p, id & 63);
         wj[j] = p;
-        idj[j] = rt_key_id(best);
+        idj[j] = id;
         wsum += p;
       }
     }
@@ -163,7 +195,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(RouteArgs A) {
 #pragma unroll
     for (int j = 0; j < SMOE_MAX_TOP_K; ++j) {
       if (j < A.k && lane == j) {
-        const float wt = A.norm ? wj[j] / wsum : wj[j];
+        const float wt = (A.norm ? wj[j] / wsum : wj[j]) * A.cfg.scale;
         const size_t o = (size_t)t * A.k + j;
         A.ids[o] = idj[j];
         A.w[o] = wt;
@@ -247,8 +279,8 @@ __global__ __launch_bounds__(GROUP_THREADS) void k_group(RouteArgs A) {
 hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int32_t* ids,
                         float* w, int32_t* user_ids, float* user_w, int group, int* meta,
                         int* active, int* offs, int* pair_token, int* pair_of,
-                        hipStream_t stream) {
-  RouteArgs A{logits, T, E, k, norm, group, ids, w, user_ids, user_w,
+                        hipStream_t stream, const RouteCfg& cfg) {
+  RouteArgs A{logits, T, E, k, norm, group, cfg, ids, w, user_ids, user_w,
               meta, active, offs, pair_token, pair_of};
   const int tpb = TOPK_THREADS / 64;
   int blocks = (T + tpb - 1) / tpb;
@@ -281,6 +313,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const int* __restrict__ pair_of,
                                                  const float* __restrict__ w,
                                                  const float* __restrict__ y_shared,
+                                                 const float* __restrict__ shared_gate,
                                                  float* __restrict__ out, int k, int d,
                                                  int accumulate) {
   const int t = blockIdx.y;
@@ -291,17 +324,20 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
     const int o = t * k + j;
     acc = fmaf(w[o], y[(size_t)pair_of[o] * d + i], acc);
   }
-  if (y_shared) acc += y_shared[(size_t)t * d + i];
+  if (y_shared) {
+    const float ys = y_shared[(size_t)t * d + i];
+    acc += shared_gate ? ys / (1.0f + expf(-shared_gate[t])) : ys;
+  }
   float* dst = out + (size_t)t * d + i;
   *dst = accumulate ? *dst + acc : acc;
 }
 
 hipError_t launch_combine(const float* y, const int* pair_of, const float* w,
-                          const float* y_shared, float* out, int T, int k, int d,
-                          int accumulate, hipStream_t stream) {
+                          const float* y_shared, const float* shared_gate, float* out, int T,
+                          int k, int d, int accumulate, hipStream_t stream) {
   dim3 grid((d + 255) / 256, T);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, stream, y, pair_of, w, y_shared, out, k, d,
-                     accumulate);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, stream, y, pair_of, w, y_shared, shared_gate,
+                     out, k, d, accumulate);
   return hipGetLastError();
 }
 

@@ -210,3 +210,26 @@ def test_trace_kernel_argument_checks():
     smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_DOWN, FAKE, FAKE)
     assert smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_NONE) == 1  # was armed, never fired
     assert smoe.smoe_trace_kernel(smoe.SMOE_KERNEL_NONE) == 0
+
+
+def test_route_options_are_validated_before_launch():
+    # "CMF v2 Format Specification", 5. Masks section: bits past the
+    # dimension must be zero; routing needs top_k routable experts
+    def call(**kw):
+        o = smoe.make_route_opts(**{k: v for k, v in kw.items() if k != "raw"})
+        for k, v in kw.get("raw", {}).items():
+            setattr(o, k, v)
+        with pytest.raises(smoe.SmoeError) as e:
+            smoe.smoe_route_ex(FAKE, 1, 8, 4, True, o, FAKE, FAKE)
+        return e.value.code
+    assert call(routable=[True] * 3 + [False] * 5) == smoe.SMOE_E_ARG      # 3 < top_k
+    o = smoe.make_route_opts(routable=[True] * 8)
+    o.expert_mask[0] |= 1 << 9                                              # past E
+    with pytest.raises(smoe.SmoeError) as e:
+        smoe.smoe_route_ex(FAKE, 1, 8, 4, True, o, FAKE, FAKE)
+    assert e.value.code == smoe.SMOE_E_ARG
+    assert call(scaling_factor=float("inf")) == smoe.SMOE_E_ARG
+    assert call(raw={"sigmoid": 2}) == smoe.SMOE_E_ARG
+    # defaults and zero tokens pass validation and launch nothing
+    smoe.smoe_route_ex(FAKE, 0, 8, 4, True, smoe.make_route_opts(), FAKE, FAKE)
+    smoe.smoe_route_ex(FAKE, 0, 8, 4, True, None, FAKE, FAKE)
