@@ -210,9 +210,11 @@ def mse_grid_scale(group_w: np.ndarray, bits: int,
     """Choose a group's scale by the 64-candidate squared-error search.
 
     Each candidate fraction * absmax is rounded to the storage dtype first;
-    the group is encoded and decoded with that stored value and the summed
-    squared error (float64) is scored; the first minimum wins. Returns
-    (stored scale as float, codes, candidate index)."""
+    the group is encoded and decoded with that stored value and the squared
+    error is summed in float64 in element order (the pages fix neither the
+    precision nor the order; a fixed order makes the choice reproducible);
+    the first minimum wins. Returns (stored scale as float, codes, candidate
+    index)."""
     st = _SCALE_DTYPES[scale_dtype]
     w = np.asarray(group_w, dtype=np.float64).reshape(-1)
     absmax = float(np.max(np.abs(w))) if w.size else 0.0
@@ -220,7 +222,10 @@ def mse_grid_scale(group_w: np.ndarray, bits: int,
     for i, frac in enumerate(candidate_fractions()):
         s = float(st(frac * absmax))
         codes = encode_codes(w, s, bits)
-        err = float(np.sum((w - decode_codes(codes, s, bits)) ** 2))
+        d = w - decode_codes(codes, s, bits)
+        err = 0.0
+        for v in (d * d).tolist():
+            err += v
         if best is None or err < best[0]:
             best = (err, s, codes, i)
     _, s, codes, i = best
