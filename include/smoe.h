@@ -250,6 +250,35 @@ int smoe_decode_step(const smoe_layer* const* layers, int n_layers, float* d_h,
                      const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
                      float eps, void* d_workspace, uint64_t ws_bytes, void* hip_stream);
 
+/* Quantiser ("SMOE Quantisation", L2-MSE Scale Optimiser; Quantisation
+ * Levels; Bit Packing): codes and group-64 scales of n_elements fp32 weights
+ * taken in their flattened order (for a [rows, cols] tensor, row-major), the
+ * same bytes a .smoe blob holds for that tensor.
+ * For every group of 64 consecutive weights (the last group may be shorter):
+ * absmax = max |w|; the 64 candidates frac_i * absmax, frac = the 64-point
+ * linspace from 0.1 to 1.0 in double, are each rounded once to the scale
+ * dtype; each candidate s encodes the group as
+ * clamp(rint(w / s * m + m), 0, 2^bits - 1) (w / s read as 0 for s == 0) and
+ * decodes it as (code - m) / m * s; its squared error is summed in double in
+ * element order, every operation rounded on its own; the first minimum wins.
+ *  d_w        device [n_elements] fp32, 4-byte aligned.
+ *  d_codes    device out, ceil(n_elements * bits / 8) bytes, codes packed
+ *             LSB-first (2 per byte for Q4, 4 for Q2); the unused high bits
+ *             of a partial last byte are 0.
+ *  d_scales   device out, ceil(n_elements / 64) values of scale_dtype
+ *             (SMOE_SCALE_F32 or SMOE_SCALE_F16), element-aligned.
+ *  n_elements at most SMOE_MAX_QUANT_ELEMENTS; a larger tensor is quantised
+ *             in pieces split at multiples of 64 elements (codes advance by
+ *             n * bits / 8 bytes, scales by n / 64 values per piece).
+ * The outputs must not overlap the input. Deterministic: the result depends
+ * on the weights only. Non-finite weights give unspecified codes and scales.
+ * Errors: SMOE_E_ARG (bits not in {2, 4}, unknown scale dtype, n_elements too
+ * large, null or misaligned pointers), SMOE_E_HIP. n_elements == 0 is a
+ * no-op. */
+#define SMOE_MAX_QUANT_ELEMENTS (1ull << 31)
+int smoe_quantise(const float* d_w, uint64_t n_elements, int bits, int scale_dtype,
+                  uint8_t* d_codes, void* d_scales, void* hip_stream);
+
 /* Kernel timing hook (instrumentation for benchmarks; not an operation of
  * the pages). Arms a one-shot pair of HIP events: the next smoe_moe_forward
  * or smoe_decode_step call that launches the chosen kernel attaches them to

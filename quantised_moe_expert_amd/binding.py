@@ -33,6 +33,7 @@ SMOE_SCALE_F16 = 1
 SMOE_MAX_TOP_K = 16
 SMOE_MAX_EXPERTS = 512
 SMOE_MAX_TOKENS = 4096
+SMOE_MAX_QUANT_ELEMENTS = 1 << 31
 
 SMOE_KERNEL_NONE = 0
 SMOE_KERNEL_GATE_UP = 1
@@ -43,7 +44,7 @@ EXPORTED = (
     "smoe_version", "smoe_last_error", "smoe_expert_layout_of", "smoe_load_blobs",
     "smoe_free", "smoe_workspace_bytes", "smoe_route", "smoe_moe_forward",
     "smoe_decode_step", "smoe_trace_kernel", "smoe_route_opts_init", "smoe_route_ex",
-    "smoe_moe_forward_ex",
+    "smoe_moe_forward_ex", "smoe_quantise",
 )
 
 
@@ -166,6 +167,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.smoe_route_ex.restype = _I
     lib.smoe_route_ex.argtypes = [_P, _I, _I, _I, _I, ctypes.POINTER(smoe_route_opts), _P, _P,
                                   _P]
+    lib.smoe_quantise.restype = _I
+    lib.smoe_quantise.argtypes = [_P, _U64, _I, _I, _P, _P, _P]
     lib.smoe_moe_forward_ex.restype = _I
     lib.smoe_moe_forward_ex.argtypes = [_P, _P, _I, _P, _I, _I, _I,
                                         ctypes.POINTER(smoe_route_opts), _P, _P, _P, _P, _U64,
@@ -276,3 +279,9 @@ def smoe_trace_kernel(kernel: int, hip_event_before: int = 0, hip_event_after: i
     if rc < 0:
         raise SmoeError(rc, smoe_last_error())
     return rc
+
+
+def smoe_quantise(d_w: int, n_elements: int, bits: int, scale_dtype: int, d_codes: int,
+                  d_scales: int, hip_stream: int = 0) -> None:
+    _check(load_library().smoe_quantise(d_w or None, n_elements, bits, scale_dtype,
+                                        d_codes or None, d_scales or None, hip_stream or None))

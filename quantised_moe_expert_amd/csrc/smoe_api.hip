@@ -434,6 +434,24 @@ int smoe_decode_step(const smoe_layer* const* layers, int n_layers, float* d_h,
   return ok();
 }
 
+int smoe_quantise(const float* d_w, uint64_t n_elements, int bits, int scale_dtype,
+                  uint8_t* d_codes, void* d_scales, void* hip_stream) {
+  if (bits != 2 && bits != 4) return fail(SMOE_E_ARG, "bits must be 2 or 4 (got %d)", bits);
+  if (scale_dtype != SMOE_SCALE_F32 && scale_dtype != SMOE_SCALE_F16)
+    return fail(SMOE_E_ARG, "unknown scale dtype %d", scale_dtype);
+  if (n_elements > SMOE_MAX_QUANT_ELEMENTS)
+    return fail(SMOE_E_ARG, "n_elements must be at most %llu (got %llu)",
+                (unsigned long long)SMOE_MAX_QUANT_ELEMENTS, (unsigned long long)n_elements);
+  if (n_elements == 0) return ok();
+  if (!d_w || !d_codes || !d_scales) return fail(SMOE_E_ARG, "null pointer argument");
+  if (!aligned(d_w, 4) || !aligned(d_scales, scale_dtype == SMOE_SCALE_F32 ? 4 : 2))
+    return fail(SMOE_E_ARG, "weights must be 4-byte and scales element-aligned");
+  int rc = check_hip(launch_quantise(d_w, (int64_t)n_elements, bits, scale_dtype == SMOE_SCALE_F16,
+                                     d_codes, d_scales, (hipStream_t)hip_stream),
+                     "quantise launch");
+  return rc ? rc : ok();
+}
+
 int smoe_trace_kernel(int kernel, void* hip_event_before, void* hip_event_after) {
   if (kernel != SMOE_KERNEL_NONE && kernel != SMOE_KERNEL_GATE_UP && kernel != SMOE_KERNEL_DOWN)
     return fail(SMOE_E_ARG, "unknown kernel id %d", kernel);

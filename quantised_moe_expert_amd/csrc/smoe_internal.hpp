@@ -105,4 +105,9 @@ hipError_t launch_combine(const float* y, const int* pair_of, const float* w,
                           const float* y_shared, const float* shared_gate, float* out, int T,
                           int k, int d, int accumulate, hipStream_t stream);
 
+// Group-64 squared-error scale search + encode + pack of n fp32 weights
+// (flattened order; a short last group is allowed).
+hipError_t launch_quantise(const float* w, int64_t n, int bits, int f16, uint8_t* codes,
+                           void* scales, hipStream_t s);
+
 }  // namespace smoe

@@ -233,3 +233,18 @@ def test_route_options_are_validated_before_launch():
     # defaults and zero tokens pass validation and launch nothing
     smoe.smoe_route_ex(FAKE, 0, 8, 4, True, smoe.make_route_opts(), FAKE, FAKE)
     smoe.smoe_route_ex(FAKE, 0, 8, 4, True, None, FAKE, FAKE)
+
+
+def test_quantise_argument_checks_before_any_launch():
+    def code(*a):
+        with pytest.raises(smoe.SmoeError) as e:
+            smoe.smoe_quantise(*a)
+        return e.value.code
+    assert code(FAKE, 64, 3, 0, FAKE, FAKE) == smoe.SMOE_E_ARG            # bits
+    assert code(FAKE, 64, 4, 2, FAKE, FAKE) == smoe.SMOE_E_ARG            # scale dtype
+    assert code(FAKE, smoe.SMOE_MAX_QUANT_ELEMENTS + 1, 4, 0, FAKE, FAKE) == smoe.SMOE_E_ARG
+    assert code(0, 64, 4, 0, FAKE, FAKE) == smoe.SMOE_E_ARG               # null weights
+    assert code(FAKE, 64, 2, 1, FAKE, 0) == smoe.SMOE_E_ARG               # null scales
+    assert code(FAKE + 2, 64, 4, 0, FAKE, FAKE) == smoe.SMOE_E_ARG        # misaligned weights
+    assert code(FAKE, 64, 4, 0, FAKE, FAKE + 2) == smoe.SMOE_E_ARG        # misaligned f32 scales
+    smoe.smoe_quantise(0, 0, 4, 0, 0, 0)                                   # empty: no-op
