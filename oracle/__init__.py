@@ -6,3 +6,4 @@ library never imports, links or calls it.
 """
 
 from .smoe_oracle import *  # noqa: F401,F403
+from . import smoe_vault  # noqa: F401
