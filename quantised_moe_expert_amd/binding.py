@@ -45,6 +45,11 @@ EXPORTED = (
     "smoe_free", "smoe_workspace_bytes", "smoe_route", "smoe_moe_forward",
     "smoe_decode_step", "smoe_trace_kernel", "smoe_route_opts_init", "smoe_route_ex",
     "smoe_moe_forward_ex", "smoe_quantise",
+    # include/smoe_vault.h
+    "smoe_arch_block_init", "smoe_vault_plan", "smoe_vault_create", "smoe_vault_put_expert",
+    "smoe_vault_finish", "smoe_vault_open", "smoe_vault_close", "smoe_vault_get_header",
+    "smoe_vault_find", "smoe_vault_layer_desc", "smoe_vault_read_expert",
+    "smoe_vault_read_layer",
 )
 
 
@@ -173,6 +178,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.smoe_moe_forward_ex.argtypes = [_P, _P, _I, _P, _I, _I, _I,
                                         ctypes.POINTER(smoe_route_opts), _P, _P, _P, _P, _U64,
                                         _P]
+    from .vault import declare as _declare_vault
+    _declare_vault(lib)
     if path is None:
         _lib = lib
     return lib

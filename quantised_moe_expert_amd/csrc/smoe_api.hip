@@ -198,6 +198,16 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
 
 }  // namespace
 
+int report_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int report_ok() { return ok(); }
+
 thread_local LaunchEvents t_launch_events;
 
 bool trace_take(int kernel, hipEvent_t* start, hipEvent_t* stop) {

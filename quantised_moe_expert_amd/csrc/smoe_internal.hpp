@@ -9,6 +9,11 @@
 
 namespace smoe {
 
+// Error reporting shared by the host translation units: sets the
+// thread-local message smoe_last_error() returns and passes code through.
+int report_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int report_ok();
+
 // How one weight matrix is walked by a wavefront: each row of W = cols*bits/32
 // 32-bit code words is split over LPR = 2^lpr_log2 lanes holding V words each
 // (W == LPR * V); a wave therefore covers 64 / LPR rows per load.

@@ -15,12 +15,12 @@ import oracle as O
 import quantised_moe_expert_amd as smoe
 from conftest import ROOT
 
-HEADER = os.path.join(ROOT, "include", "smoe.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("smoe.h", "smoe_vault.h")]
 FAKE = 1 << 40  # a 16 KB-aligned address that is never dereferenced
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(smoe_[a-z_]+)\s*\(", text)))
 
