@@ -1,6 +1,7 @@
 """Benchmark of the SMOE routed-expert MoE layer on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--copies C]
+    python bench.py --workload quantise_qwen235b_expert_q4   (the GPU quantiser)
 
 A step is one full forward of the layer (route, group, gate/up + SwiGLU, down,
 combine; a stack of layers for the stacked workload) on synthetic inputs that
@@ -57,6 +58,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload in QUANTISE_WORKLOADS:
+        bench_quantise(args)
         return
     import numpy as np
     import torch
@@ -274,6 +278,118 @@ def main():
     print(json.dumps(result), flush=True)
     for h in handles:
         smoe.smoe_free(h)
+
+
+# GPU quantiser ("SMOE Quantisation", L2-MSE Scale Optimiser): one expert's
+# three projections (gate and up [ffn, d], down [d, ffn]) per step.
+QUANTISE_WORKLOADS = {
+    "quantise_qwen235b_expert_q4": (4096, 1536, 4, "f16"),
+    "quantise_qwen235b_expert_q2": (4096, 1536, 2, "f16"),
+}
+# fp64 operations of the squared-error search per weight: for each of the 64
+# candidates, encode (divide, multiply, add, round, two clamp compares) and
+# score (subtract, divide, multiply, subtract, multiply, add)
+QUANT_OPS_PER_WEIGHT = 64 * 12
+# fp64 vector issue: 256 CUs x 64 lanes per clock x 2.4 GHz, one operation
+# per lane per clock (78.6 TFLOP/s counts a fused multiply-add as two)
+FP64_OPS_PEAK_T = 256 * 64 * 2.4e9 / 1e12
+
+
+def bench_quantise(args):
+    """Quantiser throughput: K steps, each quantising one expert (three
+    launches, fp32 weights resident in HBM, codes and scales written into an
+    expert blob); per-launch HIP events on the launch stream."""
+    import numpy as np
+    import torch
+    import synth
+    import quantised_moe_expert_amd as smoe
+
+    d, ffn, bits, sdt = QUANTISE_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    sd = smoe.SMOE_SCALE_F16 if sdt == "f16" else smoe.SMOE_SCALE_F32
+    lay = smoe.smoe_expert_layout_of(d, ffn, bits, sd)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    tensors = [lay.gate, lay.up, lay.down]
+    copies = 4
+    ws = []
+    for _ in range(copies):  # N(0, 0.02^2) weights, 1 % of them x10
+        per = []
+        for t in tensors:
+            w = torch.randn(t.rows * t.cols, device=dev, generator=gen) * 0.02
+            m = torch.rand(w.shape, device=dev, generator=gen) < 0.01
+            per.append(torch.where(m, w * 10, w))
+        ws.append(per)
+    blob = torch.zeros(lay.padded_size, dtype=torch.uint8, device=dev)
+    n_w = sum(t.rows * t.cols for t in tensors)
+
+    def step(i, evs=None):
+        for j, (t, w) in enumerate(zip(tensors, ws[i % copies])):
+            if evs is not None:
+                evs[j][0].record(stream)
+            smoe.smoe_quantise(w.data_ptr(), w.numel(), bits, sd, blob.data_ptr() + t.codes_offset,
+                               blob.data_ptr() + t.scales_offset, sh)
+            if evs is not None:
+                evs[j][1].record(stream)
+
+    steps = min(args.steps, 200)
+    for i in range(min(args.warmup, 10)):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n_l = 60
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(3)] for _ in range(n_l)]
+    for i in range(n_l):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    launch_s = sum(a.elapsed_time(b) for ev in evs for a, b in ev) * 1e-3 / (3 * n_l)
+    per_launch_ops = (n_w / 3) * QUANT_OPS_PER_WEIGHT
+    achieved = per_launch_ops / launch_s / 1e12
+    result = {
+        "metric": "quantised weights/s (GPU squared-error scale search, Qwen3-235B-shape expert)",
+        "value": round(n_w / (ms * 1e-3), 1),
+        "unit": "weights/s",
+        "n_gpus": 1, "steps": steps, "warmup": min(args.warmup, 10),
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": args.workload, "d_model": d, "ffn_dim": ffn, "bits": bits,
+                   "scale_dtype": sdt, "group_size": 64, "weights_per_step": n_w},
+        "experts_per_s": round(1e3 / ms, 2),
+        "roofline": {
+            "bound": "alu", "kernel": "k_quantise (one wave per group, one lane per candidate)",
+            "achieved": round(achieved, 3), "peak": round(FP64_OPS_PEAK_T, 2),
+            "unit": "Tops/s (fp64 vector operations)", "frac": round(achieved / FP64_OPS_PEAK_T, 4),
+            "traffic": None, "algorithmic_ops_per_launch": int(per_launch_ops),
+            "launch_us_mean": round(launch_s * 1e6, 3), "launches_timed": 3 * n_l,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        from threadpoolctl import threadpool_info
+        w0 = ws[0][0].cpu().numpy()
+        t0 = time.perf_counter()
+        n_g = 0
+        while time.perf_counter() - t0 < args.cpu_baseline_seconds and n_g < w0.size // 64:
+            O.mse_grid_scale(w0[n_g * 64:(n_g + 1) * 64], bits, sdt)
+            n_g += 1
+        dt = time.perf_counter() - t0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        result["cpu_baseline"] = {
+            "value": round(n_g * 64 / dt, 1), "unit": "weights/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_g} groups of the gate tensor through the oracle's scale search, "
+                      f"{dt:.1f} s, host cpu_count={os.cpu_count()}"}
+    print(json.dumps(result), flush=True)
 
 
 KERNEL_SOURCES = {

@@ -11,10 +11,15 @@
 //             taken as 0 when s_i == 0,
 //   error_i = sum over the group, in element order, of
 //             (w - ((code - m) / m) * s_i)^2,
-// all in double with every product, quotient and sum rounded on its own (no
-// fused multiply-add anywhere in this file); the lowest error wins, ties to
-// the lower candidate. The winner's codes are packed LSB-first (element j of
-// a byte at bit (j % per_byte) * bits).
+// all in double with every product, quotient and sum rounded on its own (the
+// compiler fuses nothing in this file); the lowest error wins, ties to the
+// lower candidate. The winner's codes are packed LSB-first (element j of a
+// byte at bit (j % per_byte) * bits).
+//
+// The result is that of the double definition bit for bit; the only shortcut
+// is that a code is decided in fp32 when an error bound shows the double
+// chain would decide the same (q_code_fast). The decoded level
+// (code - m) / m comes from a 16-entry double table computed once per wave.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -63,13 +68,40 @@ __device__ __forceinline__ double q_encode(double x, double s) {
   return c < 0.0 ? 0.0 : (c > CMAX ? CMAX : c);
 }
 
+// The code of x under scale s, decided in fp32 where that is provably the
+// same decision: t = x * (m / s) + m by one fused fp32 operation differs from
+// the double chain fl(fl(fl(x / s) * m) + m) by less than
+// 2^-22 * (|t| + 8), so rint agrees unless t lies that close to a half-integer
+// inside the clamp range; those elements (a small fraction, exact ties
+// included) take the double chain. x == 0 gives t = m exactly.
+// inv32 = m / s in fp32, +inf when that overflows (s below ~2^-125); then
+// every code of the candidate takes the double chain.
+template <int BITS>
+__device__ __forceinline__ int q_code_fast(float x32, double x64, float inv32, double s,
+                                           int c_zero) {
+  constexpr float MF = BITS == 4 ? 7.5f : 1.5f, CMAXF = (float)((1 << BITS) - 1);
+  const float t = __builtin_fmaf(x32, inv32, MF);
+  const float r = __builtin_rintf(t);
+  const float tol = 0x1p-22f * (__builtin_fabsf(t) + 8.0f);
+  const bool in_range = t > -0.5f - tol && t < CMAXF + 0.5f + tol;
+  const bool near_half = __builtin_fabsf(0.5f - __builtin_fabsf(t - r)) <= tol;
+  const bool slow = x32 != 0.0f && (inv32 == __builtin_inff() || (in_range && near_half));
+  int c = (int)__builtin_fminf(__builtin_fmaxf(r, 0.0f), CMAXF);
+  c = x32 == 0.0f ? c_zero : c;
+  if (slow) c = (int)q_encode<BITS>(x64, s);
+  return c;
+}
+
 template <int BITS, bool F16>
 __global__ __launch_bounds__(256) void k_quantise(const float* __restrict__ w, int64_t n,
                                                   uint8_t* __restrict__ codes,
                                                   void* __restrict__ scales) {
   constexpr double M = BITS == 4 ? 7.5 : 1.5;
+  constexpr int NL = 1 << BITS;
   __shared__ float s_w[4][64];
+  __shared__ double s_w64[4][64];
   __shared__ double s_err[4][64];
+  __shared__ double s_lv[4][NL];
   __shared__ uint8_t s_code[4][64];
   const int lane = threadIdx.x & 63, wl = threadIdx.x >> 6;
   const int64_t g = (int64_t)blockIdx.x * 4 + wl;
@@ -77,6 +109,8 @@ __global__ __launch_bounds__(256) void k_quantise(const float* __restrict__ w, i
   const int len = (int)(n - g * 64 < 64 ? n - g * 64 : 64);
   const float wv = lane < len ? w[g * 64 + lane] : 0.0f;
   s_w[wl][lane] = wv;
+  s_w64[wl][lane] = (double)wv;
+  if (lane < NL) s_lv[wl][lane] = ((double)lane - M) / M;  // the decoded levels
   float a = fabsf(wv);
   for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
   const double absmax = (double)a;
@@ -94,11 +128,18 @@ __global__ __launch_bounds__(256) void k_quantise(const float* __restrict__ w, i
     s = (double)f;
     sbits = __builtin_bit_cast(uint32_t, f);
   }
+  // m / s in fp32 (s is exact in fp32 for both storage dtypes); 0 for s == 0
+  // (then t = m, as the double chain reads w / s as 0)
+  const float s32 = (float)s;
+  const float inv32 = s == 0.0 ? 0.0f : (float)M / s32;
+  const int c_zero = (int)__builtin_rint(M);
   __builtin_amdgcn_wave_barrier();
   double err = 0.0;
+#pragma unroll 4
   for (int j = 0; j < len; ++j) {
-    const double x = (double)s_w[wl][j];
-    const double dec = ((q_encode<BITS>(x, s) - M) / M) * s;
+    const double x = s_w64[wl][j];
+    const int c = q_code_fast<BITS>(s_w[wl][j], x, inv32, s, c_zero);
+    const double dec = s_lv[wl][c] * s;
     const double dd = x - dec;
     err = err + dd * dd;
   }
