@@ -8,3 +8,4 @@ function names. Build with ``__graft_entry__.build()``.
 from .binding import *  # noqa: F401,F403
 from .binding import EXPORTED, LIB_PATH, SmoeError, load_library  # noqa: F401
 from .vault import *  # noqa: F401,F403
+from .offload import *  # noqa: F401,F403

@@ -50,6 +50,9 @@ EXPORTED = (
     "smoe_vault_finish", "smoe_vault_open", "smoe_vault_close", "smoe_vault_get_header",
     "smoe_vault_find", "smoe_vault_layer_desc", "smoe_vault_read_expert",
     "smoe_vault_read_layer",
+    # include/smoe_offload.h
+    "smoe_offload_create", "smoe_offload_free", "smoe_offload_forward",
+    "smoe_offload_workspace_bytes", "smoe_offload_slots", "smoe_offload_get_stats",
 )
 
 
@@ -179,7 +182,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                         ctypes.POINTER(smoe_route_opts), _P, _P, _P, _P, _U64,
                                         _P]
     from .vault import declare as _declare_vault
+    from .offload import declare as _declare_offload
     _declare_vault(lib)
+    _declare_offload(lib)
     if path is None:
         _lib = lib
     return lib

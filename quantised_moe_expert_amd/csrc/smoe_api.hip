@@ -18,9 +18,6 @@
 #include "smoe_internal.hpp"
 #include "smoe_launch.hpp"
 
-struct smoe_layer {
-  smoe::LayerInfo info;
-};
 
 namespace smoe {
 namespace {

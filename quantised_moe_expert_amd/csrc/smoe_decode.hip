@@ -81,6 +81,7 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
   DecodeArgs A{};
   A.blobs = L.blobs;
   A.stride = L.desc.blob_stride;
+  A.table = L.table;
   A.gc = P.gate.codes_off;
   A.gs = P.gate.scales_off;
   A.uc = P.up.codes_off;

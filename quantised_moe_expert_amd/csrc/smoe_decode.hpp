@@ -211,8 +211,8 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(D
   scale_groups<BITS, VG>(lrg, LPRG, sgg, tmg);
   const int j0 = my_n > 0 ? u0 / upe : 0;
   const int rg0 = u0 - j0 * upe;
-  const uint8_t* blob0 = A.blobs + (uint64_t)s_ids[j0] * A.stride;
-  const uint8_t* blob1 = A.blobs + (uint64_t)s_ids[j0 + 1 < k ? j0 + 1 : j0] * A.stride;
+  const uint8_t* blob0 = expert_blob(A.blobs, A.stride, A.table, s_ids[j0]);
+  const uint8_t* blob1 = expert_blob(A.blobs, A.stride, A.table, s_ids[j0 + 1 < k ? j0 + 1 : j0]);
   struct Batch {
     uint32_t gw[UB][VG], uw[UB][VG];
     float gs[UB][SPG::NS], us[UB][SPG::NS];
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(Deco
         hv[w][4 * i + 3] = v.w;
       }
     }
-    const uint8_t* blob = A.blobs + (uint64_t)e * A.stride;
+    const uint8_t* blob = expert_blob(A.blobs, A.stride, A.table, e);
     const uint32_t* cbase = (const uint32_t*)(blob + A.dc);
     const ST* sbase = (const ST*)(blob + A.ds);
     issue_d(dA, 0, cbase, sbase);

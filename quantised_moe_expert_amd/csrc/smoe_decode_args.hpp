@@ -24,6 +24,7 @@ constexpr int DEC_KEYS = 512;      // routing keys in LDS, padding included
 struct DecodeArgs {
   const uint8_t* blobs;  // routed expert bank, expert e at blobs + e * stride
   uint64_t stride;
+  const uint64_t* table; // optional [E] blob addresses (replaces blobs + e * stride)
   uint64_t gc, gs, uc, us, dc, ds;  // codes / scales offsets of gate, up, down
   int d, ffn, E, k, norm;
   int lg_g, lg_d;        // log2 lanes per row for the gate/up and the down rows

@@ -36,6 +36,14 @@
 
 namespace smoe {
 
+// Blob of routed expert e: base + e * stride, or table[e] when the layer runs
+// with an expert-pointer table (experts in a device cache or in host memory
+// the device can read).
+__device__ __forceinline__ const uint8_t* expert_blob(const uint8_t* base, uint64_t stride,
+                                                      const uint64_t* table, int e) {
+  return table ? (const uint8_t*)table[e] : base + (uint64_t)e * stride;
+}
+
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef u32x4 u32x4_a4 __attribute__((aligned(4)));

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemvArgs A) {
   const int gb0 = min(G, kpart * gper), gb1 = min(G, gb0 + gper);
   const int nbt = (gb1 - gb0 + GB - 1) / GB;  // batches per tile (0: an empty k-part)
   const int nb = nbt * tpw;                   // batches of this wave per chunk
-  const uint8_t* blob = A.blobs + (uint64_t)e * A.stride;
+  const uint8_t* blob = expert_blob(A.blobs, A.stride, A.table, e);
   const uint32_t* cm0 = (const uint32_t*)(blob + M0.codes_off);
   const ST* sm0 = (const ST*)(blob + M0.scales_off);
   const uint32_t* cm1 = (const uint32_t*)(blob + A.m1.codes_off);

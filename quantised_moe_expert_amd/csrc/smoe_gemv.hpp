@@ -255,7 +255,7 @@ __global__ __launch_bounds__(GV_THREADS) void k_grouped(GemvArgs A) {
   const int rw0 = (blockIdx.x * GV_WAVES + wave) * rpw;
   const int ngroups = rw0 < rows ? (min(rw0 + rpw, rows) - rw0 + RPW - 1) / RPW : 0;
   const int Wr = M0.words_per_row, G = M0.cols / 64;
-  const uint8_t* blob = A.blobs + (uint64_t)e * A.stride;
+  const uint8_t* blob = expert_blob(A.blobs, A.stride, A.table, e);
   const uint32_t* c0 = (const uint32_t*)(blob + M0.codes_off);
   const ST* s0 = (const ST*)(blob + M0.scales_off);
   const uint32_t* c1 = (const uint32_t*)(blob + A.m1.codes_off);

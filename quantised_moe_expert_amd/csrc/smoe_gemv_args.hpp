@@ -68,6 +68,7 @@ struct MatArgs {
 struct GemvArgs {
   const uint8_t* blobs;  // routed bank (or the shared blob)
   uint64_t stride;
+  const uint64_t* table; // optional [E] blob addresses (routed experts only)
   int shared;            // 1: one expert (the shared one), all tokens, pair = token
   int T;
   MatArgs m0, m1;        // gate/up (m1 used by the gate/up stage only)

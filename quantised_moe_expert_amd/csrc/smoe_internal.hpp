@@ -47,6 +47,7 @@ struct LayerInfo {
   smoe_layer_desc desc;
   const uint8_t* blobs;
   uint64_t nbytes;
+  const uint64_t* table;   // optional device [E] blob addresses (host offload)
   const uint8_t* shared;
   uint64_t shared_nbytes;
   ExpertPlan plan;
@@ -116,3 +117,8 @@ hipError_t launch_quantise(const float* w, int64_t n, int bits, int f16, uint8_t
                            void* scales, hipStream_t s);
 
 }  // namespace smoe
+
+// The opaque handle of include/smoe.h: host-side metadata of one layer.
+struct smoe_layer {
+  smoe::LayerInfo info;
+};

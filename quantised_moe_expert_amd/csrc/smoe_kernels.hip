@@ -470,6 +470,7 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
   GemvArgs A{};
   A.blobs = shared ? L.shared : L.blobs;
   A.stride = shared ? 0 : L.desc.blob_stride;
+  A.table = shared ? nullptr : L.table;
   A.shared = shared;
   A.T = T;
   A.m0 = mat_args(P.gate);
@@ -510,6 +511,7 @@ hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, i
   GemvArgs A{};
   A.blobs = shared ? L.shared : L.blobs;
   A.stride = shared ? 0 : L.desc.blob_stride;
+  A.table = shared ? nullptr : L.table;
   A.shared = shared;
   A.T = T;
   A.m0 = mat_args(P.down);

@@ -15,7 +15,7 @@ import oracle as O
 import quantised_moe_expert_amd as smoe
 from conftest import ROOT
 
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("smoe.h", "smoe_vault.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("smoe.h", "smoe_vault.h", "smoe_offload.h")]
 FAKE = 1 << 40  # a 16 KB-aligned address that is never dereferenced
 
 
