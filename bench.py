@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--copies C]
     python bench.py --workload quantise_qwen235b_expert_q4   (the GPU quantiser)
+    python bench.py --workload qwen235b_q4_b1_offload_direct  (experts in host memory)
 
 A step is one full forward of the layer (route, group, gate/up + SwiGLU, down,
 combine; a stack of layers for the stacked workload) on synthetic inputs that
@@ -44,6 +45,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--trace-launches", type=int, default=400,
                     help="forwards per kernel in the per-launch timing pass (0 = skip)")
+    ap.add_argument("--offload-slots", type=int, default=-1,
+                    help="host-offload workloads: device cache slots (0 = direct reads; "
+                         "-1 = the workload's default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -61,6 +65,9 @@ def main():
         return
     if args.workload in QUANTISE_WORKLOADS:
         bench_quantise(args)
+        return
+    if args.workload in OFFLOAD_WORKLOADS:
+        bench_offload(args)
         return
     import numpy as np
     import torch
@@ -390,6 +397,121 @@ def bench_quantise(args):
             "sample": f"{n_g} groups of the gate tensor through the oracle's scale search, "
                       f"{dt:.1f} s, host cpu_count={os.cpu_count()}"}
     print(json.dumps(result), flush=True)
+
+
+# Host offload: the one-token Qwen3-235B-shape Q4 layer with its 128 experts in
+# pinned host memory (1.36 GB), new routing every step; (workload, default
+# cache slots): 0 = the kernels read the experts over PCIe, > 0 = an LRU
+# device cache of that many blobs, misses copied by DMA.
+OFFLOAD_WORKLOADS = {
+    "qwen235b_q4_b1_offload_direct": 0,
+    "qwen235b_q4_b1_offload_cache32": 32,
+}
+# PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 coding
+PCIE_PEAK_GBPS = 32 * 16 * 128 / 130 / 8
+
+
+def bench_offload(args):
+    import torch
+    import synth
+    import quantised_moe_expert_amd as smoe
+
+    W = synth.WORKLOADS["qwen235b_q4_b1"]
+    slots = OFFLOAD_WORKLOADS[args.workload] if args.offload_slots < 0 else args.offload_slots
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    lay = smoe.smoe_expert_layout_of(W.d_model, W.ffn_dim, W.bits, smoe.SMOE_SCALE_F32)
+    stride, raw, E, k = lay.padded_size, lay.raw_size, W.num_experts, W.top_k
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    host = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
+    for e in range(E):  # uniform code bytes, lognormal fp32 scales, zero padding
+        b = torch.randint(0, 256, (stride,), dtype=torch.uint8, device=dev, generator=gen)
+        for t in (lay.gate, lay.up, lay.down):
+            sc = b[t.scales_offset: t.scales_offset + t.scales_bytes].view(torch.float32)
+            sc.copy_(torch.empty(sc.shape, device=dev).log_normal_(math.log(0.02), 0.5,
+                                                                   generator=gen))
+        b[raw:] = 0
+        host[e].copy_(b)
+    torch.cuda.synchronize()
+    cache = torch.empty(max(slots, 1) * stride, dtype=torch.uint8, device=dev)
+    table = torch.zeros(E, dtype=torch.int64, device=dev)
+    desc = smoe.make_desc(W.d_model, W.ffn_dim, E, W.bits, stride, smoe.SMOE_SCALE_F32)
+    off = smoe.smoe_offload_create(desc, host.data_ptr(), host.numel(), 0, 0,
+                                   cache.data_ptr() if slots else 0, slots * stride,
+                                   table.data_ptr())
+    n_sets = 64
+    lg = torch.randn((n_sets, 1, E), device=dev, generator=gen)
+    x = torch.randn((1, W.d_model), device=dev, generator=gen).to(torch.bfloat16)
+    out = torch.empty((1, W.d_model), dtype=torch.float32, device=dev)
+    nws = smoe.smoe_offload_workspace_bytes(off, 1, k)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        smoe.smoe_offload_forward(off, x.data_ptr(), smoe.SMOE_DTYPE_BF16, lg[i % n_sets].data_ptr(),
+                                  1, k, True, out.data_ptr(), 0, 0, ws.data_ptr(), nws, sh)
+
+    steps = min(args.steps, 500)
+    warm = min(args.warmup, 50)
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    st0 = smoe.smoe_offload_get_stats(off)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(warm + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    st1 = smoe.smoe_offload_get_stats(off)
+    ms = e0.elapsed_time(e1) / steps
+    # bytes over PCIe per step: every selected expert (direct) or the misses
+    # (copied) plus the experts read directly for want of a slot
+    if slots == 0:
+        pcie_bytes = k * raw
+    else:
+        pcie_bytes = ((st1.bytes_fetched - st0.bytes_fetched)
+                      + (st1.direct - st0.direct) * raw) / steps
+    achieved = pcie_bytes / (ms * 1e-3) / 1e9
+    # a plain 256 MiB pinned host -> device copy: what the link gives a DMA
+    src = torch.empty(1 << 28, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        dst.copy_(src, non_blocking=True)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src, non_blocking=True)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 5 * (1 << 28) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    hits = st1.hits - st0.hits
+    fetched = st1.fetched - st0.fetched
+    result = {
+        "metric": "MoE-layer tokens/s with the routed experts in host memory (PCIe GB/s)",
+        "value": round(1e3 / ms, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": args.workload, "d_model": W.d_model, "ffn_dim": W.ffn_dim,
+                   "num_experts": E, "top_k": k, "n_tokens": 1, "bits": W.bits,
+                   "scale_dtype": "f32", "cache_slots": slots,
+                   "host_bank_bytes": E * stride},
+        "pcie_bytes_per_step": int(pcie_bytes),
+        "cache_hit_rate": round(hits / max(1, hits + fetched + (st1.direct - st0.direct)), 4),
+        "copy_GBps_measured": round(copy_gbps, 2),
+        "wall_s_timed": round(t_wall, 3),
+        "roofline": {
+            "bound": "pcie", "kernel": "whole forward (host-to-device traffic)",
+            "achieved": round(achieved, 2), "peak": round(PCIE_PEAK_GBPS, 2), "unit": "GB/s",
+            "frac": round(achieved / PCIE_PEAK_GBPS, 4), "traffic": None,
+        },
+    }
+    print(json.dumps(result), flush=True)
+    smoe.smoe_offload_free(off)
 
 
 KERNEL_SOURCES = {

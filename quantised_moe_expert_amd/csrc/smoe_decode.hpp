@@ -83,7 +83,9 @@ __device__ __forceinline__ float block_sum(float v, float* s_tmp) {
 
 // --------------------------------------------------------------------- K1 --
 
-template <int BITS, typename ST, int VG, bool XF32>
+// TBL: experts addressed through A.table (host offload); a template
+// parameter so that the resident-bank kernels carry no trace of it.
+template <int BITS, typename ST, int VG, bool XF32, bool TBL>
 __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(DecodeArgs A) {
   constexpr int PPW = QT<BITS>::PPW;
   constexpr int WPW = QT<BITS>::WPW;
@@ -211,8 +213,9 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(D
   scale_groups<BITS, VG>(lrg, LPRG, sgg, tmg);
   const int j0 = my_n > 0 ? u0 / upe : 0;
   const int rg0 = u0 - j0 * upe;
-  const uint8_t* blob0 = expert_blob(A.blobs, A.stride, A.table, s_ids[j0]);
-  const uint8_t* blob1 = expert_blob(A.blobs, A.stride, A.table, s_ids[j0 + 1 < k ? j0 + 1 : j0]);
+  const uint64_t* table = TBL ? A.table : nullptr;
+  const uint8_t* blob0 = expert_blob(A.blobs, A.stride, table, s_ids[j0]);
+  const uint8_t* blob1 = expert_blob(A.blobs, A.stride, table, s_ids[j0 + 1 < k ? j0 + 1 : j0]);
   struct Batch {
     uint32_t gw[UB][VG], uw[UB][VG];
     float gs[UB][SPG::NS], us[UB][SPG::NS];
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(D
 
 // --------------------------------------------------------------------- K2 --
 
-template <int BITS, typename ST, int VD>
+template <int BITS, typename ST, int VD, bool TBL>
 __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(DecodeArgs A) {
   constexpr int PPW = QT<BITS>::PPW;
   constexpr int WPW = QT<BITS>::WPW;
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(Deco
         hv[w][4 * i + 3] = v.w;
       }
     }
-    const uint8_t* blob = expert_blob(A.blobs, A.stride, A.table, e);
+    const uint8_t* blob = expert_blob(A.blobs, A.stride, TBL ? A.table : nullptr, e);
     const uint32_t* cbase = (const uint32_t*)(blob + A.dc);
     const ST* sbase = (const ST*)(blob + A.ds);
     issue_d(dA, 0, cbase, sbase);
@@ -475,12 +478,18 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(Deco
 
 template <int BITS, typename ST, int VG, bool XF32>
 hipError_t launch_dec_gate_up(const DecodeArgs& A, int nwg, hipStream_t s) {
-  return launch_kernel(k_dec_gate_up<BITS, ST, VG, XF32>, dim3(nwg), dim3(DEC_THREADS), s, A);
+  if (A.table)
+    return launch_kernel(k_dec_gate_up<BITS, ST, VG, XF32, true>, dim3(nwg), dim3(DEC_THREADS), s,
+                         A);
+  return launch_kernel(k_dec_gate_up<BITS, ST, VG, XF32, false>, dim3(nwg), dim3(DEC_THREADS), s,
+                       A);
 }
 
 template <int BITS, typename ST, int VD>
 hipError_t launch_dec_down(const DecodeArgs& A, int nwg, hipStream_t s) {
-  return launch_kernel(k_dec_down<BITS, ST, VD>, dim3(nwg), dim3(DEC_THREADS), s, A);
+  if (A.table)
+    return launch_kernel(k_dec_down<BITS, ST, VD, true>, dim3(nwg), dim3(DEC_THREADS), s, A);
+  return launch_kernel(k_dec_down<BITS, ST, VD, false>, dim3(nwg), dim3(DEC_THREADS), s, A);
 }
 
 }  // namespace smoe

@@ -39,9 +39,13 @@ namespace smoe {
 // Blob of routed expert e: base + e * stride, or table[e] when the layer runs
 // with an expert-pointer table (experts in a device cache or in host memory
 // the device can read).
+// A table entry is cast through the global address space so that the loads
+// from the blob stay global loads (a plain pointer read from memory would be
+// generic and turn every weight load into a flat load).
 __device__ __forceinline__ const uint8_t* expert_blob(const uint8_t* base, uint64_t stride,
                                                       const uint64_t* table, int e) {
-  return table ? (const uint8_t*)table[e] : base + (uint64_t)e * stride;
+  typedef const __attribute__((address_space(1))) uint8_t* global_bytes;
+  return table ? (const uint8_t*)(global_bytes)table[e] : base + (uint64_t)e * stride;
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
