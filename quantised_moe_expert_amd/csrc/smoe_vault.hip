@@ -323,6 +323,8 @@ int validate(smoe_vault* v) {
       if (d[k].ndim != 2) BAD("entry %llu: descriptor %d is not 2-D", (unsigned long long)i, k);
       if (d[k].reserved_0[0] || d[k].reserved_0[1]) BAD("entry %llu: descriptor %d reserved bytes are not zero", (unsigned long long)i, k);
       const uint64_t cnt = (uint64_t)d[k].rows * d[k].cols;
+      if (cnt > (1ull << 48))  // keeps the size arithmetic below exact
+        BAD("entry %llu: descriptor %d shape is implausibly large", (unsigned long long)i, k);
       if (d[k].packed_size != ceil_div(cnt * h.bits, 8))
         BAD("entry %llu: descriptor %d packed_size is not ceil(rows*cols*bits/8)", (unsigned long long)i, k);
       if (d[k].scales_size != ceil_div(cnt, SMOE_GROUP_SIZE) * 2)

@@ -371,3 +371,16 @@ def test_writer_argument_checks(tmp_path):
     with pytest.raises(smoe.SmoeError) as e:
         smoe.smoe_vault_finish(w)   # three experts missing
     assert e.value.code == smoe.SMOE_E_ARG
+
+
+def test_huge_descriptor_shape_is_refused_without_overflow(tmp_path):
+    # rows * cols near 2^64 would wrap a 64-bit size computation
+    bad = _patch(_valid(), V.DESC_FIELDS, 64 + 48 * 6, "rows", 0xFFFFFFFF)
+    bad = _patch(bad, V.DESC_FIELDS, 64 + 48 * 6, "cols", 0xFFFFFFFF)
+    with pytest.raises(V.VaultFormatError):
+        V.read_vault(bad)
+    p = tmp_path / "huge.smoe"
+    p.write_bytes(bad)
+    with pytest.raises(smoe.SmoeError) as e:
+        smoe.smoe_vault_open(str(p))
+    assert e.value.code == smoe.SMOE_E_FORMAT
