@@ -118,6 +118,14 @@ WsLayout ws_layout(const LayerInfo& L, int T, int k) {
   W.y = take(P * L.desc.d_model * 4);
   W.h_shared = take((uint64_t)T * L.desc.shared_ffn_dim * 4);
   W.y_shared = take(L.desc.shared_ffn_dim ? (uint64_t)T * L.desc.d_model * 4 : 0);
+  const uint64_t slots = P < E ? P : E;
+  W.prep_bytes = 0;
+  if (gmk_wanted((int)P, (int)slots)) {
+    const uint64_t gu = gmk_prep_bytes((uint64_t)T, (int)L.desc.d_model);
+    const uint64_t dn = gmk_prep_bytes(P, (int)L.desc.ffn_dim);
+    W.prep_bytes = gu > dn ? gu : dn;
+  }
+  W.prep = take(W.prep_bytes);
   W.total = o;
   return W;
 }
@@ -165,7 +173,7 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
   {
     TracedLaunch t(SMOE_KERNEL_GATE_UP);
     rc = check_hip(launch_gate_up(L, false, x, xmode, eps, T, T * k, max_slots, meta, active, offs,
-                                  pair_token, h, s),
+                                  pair_token, h, s, W.prep_bytes ? ws + W.prep : nullptr),
                    "gate/up launch");
   }
   if (rc) return rc;
@@ -174,16 +182,17 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
     float* hsh = (float*)(ws + W.h_shared);
     ysh = (float*)(ws + W.y_shared);
     if ((rc = check_hip(launch_gate_up(L, true, x, xmode, eps, T, T, 1, meta, active, offs,
-                                       pair_token, hsh, s),
+                                       pair_token, hsh, s, nullptr),
                         "shared gate/up launch")))
       return rc;
-    if ((rc = check_hip(launch_down(L, true, hsh, T, T, 1, meta, active, offs, ysh, s),
+    if ((rc = check_hip(launch_down(L, true, hsh, T, T, 1, meta, active, offs, ysh, s, nullptr),
                         "shared down launch")))
       return rc;
   }
   {
     TracedLaunch t(SMOE_KERNEL_DOWN);
-    rc = check_hip(launch_down(L, false, h, T, T * k, max_slots, meta, active, offs, y, s),
+    rc = check_hip(launch_down(L, false, h, T, T * k, max_slots, meta, active, offs, y, s,
+                               W.prep_bytes ? ws + W.prep : nullptr),
                    "down launch");
   }
   if (rc) return rc;

@@ -504,6 +504,284 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemvArgs A) {
   }
 }
 
+// ------------------------------------------------- K-sliced (prefill) stage
+//
+// For slots with many tokens (prefill-sized batches) each weight fetch
+// should serve more tokens than one MFMA's 16, but a 4096-wide token vector
+// takes 8 KB of LDS as fp16, so 64 tokens do not fit whole. This stage takes
+// the chunk's 64 tokens one K slice (eight scale groups, 512 weights) at a
+// time into one of two LDS buffers and feeds every decoded weight operand to
+// four MFMA token tiles, so a slot's weights are read once per 64 tokens
+// instead of once per 16.
+//   - The token vectors were converted beforehand (k_gmk_prep) into the
+//     fp16 pairs, group offsets K and output factors of k_gemm's staging,
+//     stored per vector in the order of the MFMA operand, so a slice is
+//     copied global -> LDS with direct-to-LDS loads (global_load_lds_dwordx4:
+//     lane i writes 16 bytes at LDS base + 16 i; lane = token), no
+//     registers and no conversion in this kernel.
+//   - Each wave owns one 16-row tile of one matrix: for gate/up, waves 0-3
+//     take four gate tiles and waves 4-7 the up tiles of the same 64 rows
+//     (their results meet in LDS for SwiGLU); for down, eight tiles.
+//   - Per slice: the next slice's weights, then its tokens (into the other
+//     buffer), are loaded before the current slice is multiplied; a wait for
+//     all of the wave's loads and one barrier end the slice.
+
+template <int BITS, typename ST, bool GU, bool SV>
+__global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
+  extern __shared__ uint32_t lds[];
+  constexpr int WPG = QT<BITS>::WPG, HALVES = QT<BITS>::PPW / 4;
+  // two 16-row tiles per wave where the scales come as vector quads; one
+  // otherwise (per-group scale registers would not fit beside two tiles)
+  constexpr int TC = GMK_TC, NTT = TC / 16, KSG = GMK_KSG, GB = KSG, TPW = gmk_tpw(SV);
+  static_assert(TC == 64, "one direct-to-LDS load per token per lane");
+  constexpr int QPS = KSG * WPG * HALVES;  // 16-byte pair quads of a slice per token
+  static_assert(QPS == 64, "a slice is 512 weights");
+  constexpr int XB = QPS * TC * 4, KB = KSG * TC;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = blockIdx.y;
+  if (slot >= A.meta[0]) return;  // workgroup-uniform
+  const int e = A.active[slot], p0 = A.offs[slot], p1 = A.offs[slot + 1];
+  if (p0 >= p1) return;
+  const int mat = GU ? wave >> 2 : 0;  // 0: gate (or down), 1: up
+  const int tw = GU ? wave & 3 : wave;  // tile pair of the wave within the block
+  const MatArgs& M = mat ? A.m1 : A.m0;
+  const int rows = M.rows, Wr = M.words_per_row, cols = M.cols, G = cols / 64;
+  const int NSL = (G + KSG - 1) / KSG;
+  const int r = lane & 15, b = lane >> 4;
+  const uint8_t* blob = expert_blob(A.blobs, A.stride, A.table, e);
+  int row[TPW];
+  const uint32_t* cw0[TPW];
+  const ST* sw0[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    row[u] = ((blockIdx.x * (GU ? 4 : GMK_NW) + tw) * TPW + u) * 16 + r;
+    const int rc = min(row[u], rows - 1);
+    cw0[u] = (const uint32_t*)(blob + M.codes_off) + (size_t)rc * Wr;
+    sw0[u] = (const ST*)(blob + M.scales_off) + (size_t)rc * G;
+  }
+  const GmkLds L = gmk_lds_layout();
+  uint32_t* X = lds + L.x;
+  float* Kl = (float*)(lds + L.k);
+  float* osc = (float*)(lds + L.osc);
+  uint32_t magic;
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  const int wmap = BITS == 4 ? (b & 1) * 4 + (b >> 1) * 2 : b;
+  constexpr int UG = BITS == 4 ? 2 : 4;
+  constexpr int NU = GB / UG;
+  static_assert(GB == 8, "one scale load per lane covers a slice of eight groups");
+  // prepared vectors: pair quads [V][cols / 8] (16 bytes each), K [V][G],
+  // output factors [V]
+  const u32x4* xq = (const u32x4*)A.prep_x;
+  const float* xk = A.prep_k;
+  const float* xo = A.prep_o;
+
+  struct Batch {
+    u32x4 w[TPW][NU];
+    u32x4 sq[TPW];
+    float s[TPW][SV ? 1 : GB];
+  };
+  auto load = [&](Batch& B, int sl) {  // slice sl (clamped) of this lane's rows
+    const int g0 = min(sl, NSL - 1) * KSG;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) B.w[t][u] = gm_unit_load<BITS>(cw0[t], g0 + u * UG, G, b);
+      if constexpr (SV) {
+        B.sq[t] = gm_scale_quad<ST>(sw0[t], min(g0 + 4 * (b & 1), G - 4));
+      } else {
+#pragma unroll
+        for (int j = 0; j < GB; ++j) B.s[t][j] = load_scale<ST, false>(sw0[t] + min(g0 + j, G - 1));
+      }
+    }
+  };
+  // SV: quarters 0 and 2 loaded quad 0 of the slice, 1 and 3 quad 1
+  auto scales = [&](const Batch& B, int t, float* sc) {
+    if constexpr (SV) {
+      uint32_t q[4] = {B.sq[t].x, B.sq[t].y, B.sq[t].z, B.sq[t].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t lo = q[i], hi = q[i];
+        swap16(lo, hi);  // lo: quad 0, hi: quad 1 (in every quarter)
+        sc[i] = __builtin_bit_cast(float, lo);
+        sc[4 + i] = __builtin_bit_cast(float, hi);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < GB; ++j) sc[j] = B.s[t][j];
+    }
+  };
+  auto word = [&](const uint32_t (*w)[4], int j, int h) -> uint32_t {
+    if constexpr (BITS == 4) return w[j / 2][(j % 2) * 2 + h];
+    return w[j / 4][j % 4];
+  };
+  // this lane's token of the chunk (clamped) as a prepared-vector index
+  auto vec_of = [&](int pc, int nt) {
+    const int p = pc + min(lane, nt - 1);
+    return GU ? A.pair_token[p] : p;
+  };
+  // tokens of slice sl (clamped) into buffer buf: wave w copies quads
+  // w * 8 .. w * 8 + 7 of the slice for all 64 tokens, and the offsets of
+  // group w
+  auto stage = [&](int v, int sl, int buf) {
+    const int s = min(sl, NSL - 1);
+    const u32x4* src = xq + (size_t)v * (cols / 8) + (size_t)s * QPS;
+#pragma unroll
+    for (int i = 0; i < QPS / GMK_NW; ++i) {
+      const int qd = wave * (QPS / GMK_NW) + i;
+      // a slice past the row's end (G not a multiple of 8) re-reads the
+      // row's last quads; those entries are never used
+      const int qc = min(s * QPS + qd, cols / 8 - 1) - s * QPS;
+      __builtin_amdgcn_global_load_lds((const void*)(src + qc),
+                                       (__attribute__((address_space(3))) void*)(X + buf * XB +
+                                                                                 qd * TC * 4),
+                                       16, 0, 0);
+    }
+    const int g = min(s * KSG + wave, G - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(xk + (size_t)v * G + g),
+                                     (__attribute__((address_space(3))) void*)(Kl + buf * KB +
+                                                                               wave * TC),
+                                     4, 0, 0);
+  };
+
+  f32x4m acc[TPW][NTT];
+  auto compute = [&](const Batch& B, int sl, int buf) {
+    const int g0 = sl * KSG;
+    const int glast = min(G - 1 - g0, KSG - 1);
+    uint32_t w[TPW][NU][4];
+    float sc[TPW][GB];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      scales(B, t, sc[t]);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) gm_unit_arrange<BITS>(B.w[t][u], w[t][u]);
+    }
+    const uint32_t* Xb = X + buf * XB;
+    const float* Kb = Kl + buf * KB;
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      const bool own = g0 + j < G;  // wave-uniform
+      const int gl = min(j, glast);
+      h8 op[2][TPW];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+          op[h][u] = gm_operand<BITS>(word(w[u], j, BITS == 4 ? h : 0), BITS == 4 ? 0 : h, magic);
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) {
+        f32x4m d[TPW];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) d[u] = f32x4m{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int hv = BITS == 4 ? 0 : h;
+          const int qd = BITS == 4 ? (gl * WPG + wmap + h) : (gl * WPG + wmap) * HALVES + hv;
+          const h8 av = __builtin_bit_cast(h8, *(const u32x4*)(Xb + (qd * TC + 16 * t + r) * 4));
+#pragma unroll
+          for (int u = 0; u < TPW; ++u)
+            d[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, op[h][u], d[u], 0, 0, 0);
+        }
+        const f32x4m kv = *(const f32x4m*)(Kb + gl * TC + 16 * t + 4 * b);
+        const float k0 = kv.x, k1 = kv.y, k2 = kv.z, k3 = kv.w;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const float sj = own ? sc[u][j] : 0.f;
+          const float a0 = d[u].x, a1 = d[u].y, a2 = d[u].z, a3 = d[u].w;
+          acc[u][t].x = fmaf(sj, a0 - k0, acc[u][t].x);
+          acc[u][t].y = fmaf(sj, a1 - k1, acc[u][t].y);
+          acc[u][t].z = fmaf(sj, a2 - k2, acc[u][t].z);
+          acc[u][t].w = fmaf(sj, a3 - k3, acc[u][t].w);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  Batch bA, bB;
+  for (int pc = p0; pc < p1; pc += TC) {
+    const int nt = min(TC, p1 - pc);
+    if (pc > p0) __syncthreads();  // the previous chunk's LDS readers are done
+    const int v = vec_of(pc, nt);
+    load(bA, 0);
+    stage(v, 0, 0);
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds((const void*)(xo + v),
+                                       (__attribute__((address_space(3))) void*)osc, 4, 0, 0);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) acc[u][t] = f32x4m{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // slices in pairs; every load of the next slice is issued before the
+    // current one is multiplied, and complete before the barrier
+    for (int sl = 0; sl < NSL; sl += 2) {
+      load(bB, sl + 1);
+      stage(v, sl + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(bA, sl, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (sl + 1 >= NSL) break;
+      load(bA, sl + 2);
+      stage(v, sl + 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(bB, sl + 1, 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    // outputs: lane (r, b) holds tokens 16t + 4b .. + 3 of its rows
+    if constexpr (GU) {
+      // the up waves hand their sums to the gate waves of the same tiles
+      float* xch = (float*)X;  // buffer 0 is free after the last barrier
+      if (mat == 1) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+          for (int t = 0; t < NTT; ++t)
+            *(f32x4m*)(xch + (((tw * TPW + u) * NTT + t) * 64 + lane) * 4) = acc[u][t];
+      }
+      __syncthreads();
+      if (mat == 0) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          if (row[u] >= rows) continue;
+#pragma unroll
+          for (int t = 0; t < NTT; ++t) {
+            const f32x4m up = *(const f32x4m*)(xch + (((tw * TPW + u) * NTT + t) * 64 + lane) * 4);
+            const float ga[4] = {acc[u][t].x, acc[u][t].y, acc[u][t].z, acc[u][t].w};
+            const float ua[4] = {up.x, up.y, up.z, up.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int tk = 16 * t + 4 * b + i;
+              if (tk < nt) {
+                const float o = osc[tk];
+                const float gg = ga[i] * o, uu = ua[i] * o;
+                A.out[(size_t)(pc + tk) * rows + row[u]] = gg / (1.0f + expf(-gg)) * uu;
+              }
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        if (row[u] >= rows) continue;
+#pragma unroll
+        for (int t = 0; t < NTT; ++t) {
+          const float va[4] = {acc[u][t].x, acc[u][t].y, acc[u][t].z, acc[u][t].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tk = 16 * t + 4 * b + i;
+            if (tk < nt) A.out[(size_t)(pc + tk) * rows + row[u]] = va[i] * osc[tk];
+          }
+        }
+      }
+    }
+  }
+}
+
 // Launcher, instantiated per (BITS, scale type) in smoe_gemm_inst.hip.
 // Workgroups of more than 64 KB of LDS need the kernel's limit raised.
 template <typename K>
@@ -524,6 +802,20 @@ static hipError_t launch_gm_nw(const GemvArgs& A, bool gate_up, int in, dim3 gri
   if (!gate_up) return go(k_gemm<BITS, ST, GV_F32, false, SV, NW>);
   if (in == GV_BF16) return go(k_gemm<BITS, ST, GV_BF16, true, SV, NW>);
   return go(k_gemm<BITS, ST, GV_F32_SPLIT, true, SV, NW>);
+}
+
+template <int BITS, typename ST>
+hipError_t launch_gm_ks(const GemvArgs& A, bool gate_up, dim3 grid, hipStream_t s) {
+  const unsigned lds = (unsigned)gmk_lds_layout().total * 4;
+  const dim3 block(GMK_NW * 64);
+  const bool sv = A.m0.cols / 64 % 4 == 0;
+  auto go = [&](auto kernel) {
+    const hipError_t e = gm_allow_lds(kernel, lds);
+    return e != hipSuccess ? e : launch_kernel_lds(kernel, grid, block, lds, s, A);
+  };
+  if (gate_up)
+    return sv ? go(k_gemm_ks<BITS, ST, true, true>) : go(k_gemm_ks<BITS, ST, true, false>);
+  return sv ? go(k_gemm_ks<BITS, ST, false, true>) : go(k_gemm_ks<BITS, ST, false, false>);
 }
 
 template <int BITS, typename ST>

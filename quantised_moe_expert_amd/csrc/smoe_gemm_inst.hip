@@ -11,5 +11,7 @@ namespace smoe {
 
 template hipError_t launch_gm<SMOE_INST_BITS, SMOE_INST_ST>(const GemvArgs&, bool, int, int,
                                                             dim3, unsigned, hipStream_t);
+template hipError_t launch_gm_ks<SMOE_INST_BITS, SMOE_INST_ST>(const GemvArgs&, bool, dim3,
+                                                               hipStream_t);
 
 }  // namespace smoe

@@ -60,6 +60,32 @@ __host__ __device__ inline GmLds gm_lds_layout(int cols, int tc, bool split, int
   return L;
 }
 
+// K-sliced matrix-core stage (k_gemm_ks): shape and LDS layout.
+constexpr int GMK_NW = 8;   // waves per workgroup, one 16-row tile each
+constexpr int GMK_TC = 64;  // tokens per chunk: four MFMA token tiles
+constexpr int GMK_KSG = 8;  // scale groups per K slice
+// 16-row tiles per wave: two when every row holds whole quads of scale
+// groups (vector scale loads), else one
+__host__ __device__ constexpr int gmk_tpw(bool sv) { return sv ? 2 : 1; }
+// rows of one matrix per workgroup: gate/up 4 waves per matrix, down 8
+__host__ __device__ constexpr int gmk_rows_per_block(bool gate_up, bool sv) {
+  return (gate_up ? 4 : GMK_NW) * gmk_tpw(sv) * 16;
+}
+
+struct GmkLds {
+  int x, k, s, osc, total;  // offsets and size in 32-bit words
+};
+
+__host__ __device__ inline GmkLds gmk_lds_layout() {
+  GmkLds L;
+  L.x = 0;                                     // 2 buffers of KSG * 32 * TC pairs
+  L.k = L.x + 2 * GMK_KSG * 32 * GMK_TC;       // 2 buffers of KSG * TC offsets
+  L.s = L.k + 2 * GMK_KSG * GMK_TC;            // per-token power-of-two scale
+  L.osc = L.s + GMK_TC;                        // per-token output factor
+  L.total = L.osc + GMK_TC;
+  return L;
+}
+
 struct MatArgs {
   uint64_t codes_off, scales_off;
   int rows, cols, words_per_row, lpr_log2;
@@ -85,6 +111,11 @@ struct GemvArgs {
   const int* offs;
   const int* pair_token;
   float* out;            // gate/up: h [pairs, rows]; down: y [pairs, rows]
+  // K-sliced stage: activation vectors prepared by k_gmk_prep (fp16 pair
+  // quads [V][cols / 8], group offsets [V][cols / 64], output factors [V])
+  const uint32_t* prep_x;
+  const float* prep_k;
+  const float* prep_o;
 };
 
 // Launchers, defined in smoe_gemv.hpp and instantiated per (BITS, scale
@@ -99,5 +130,10 @@ hipError_t launch_dn(const GemvArgs& A, dim3 grid, unsigned lds, hipStream_t s);
 template <int BITS, typename ST>
 hipError_t launch_gm(const GemvArgs& A, bool gate_up, int in, int nw, dim3 grid, unsigned lds,
                      hipStream_t s);
+// K-sliced matrix-core stage for slots of many tokens (64 per chunk, 8 waves,
+// one 16-row tile per wave); routed experts, bf16 tokens (gate/up) or fp32 h
+// (down). Grid (ceil(rows / 128), slots).
+template <int BITS, typename ST>
+hipError_t launch_gm_ks(const GemvArgs& A, bool gate_up, dim3 grid, hipStream_t s);
 
 }  // namespace smoe

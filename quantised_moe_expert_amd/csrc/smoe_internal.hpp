@@ -40,8 +40,15 @@ bool plan_matrix(int rows, int cols, int bits, uint64_t codes_off, uint64_t scal
 struct WsLayout {
   uint64_t ids, w, meta, active, offs, pair_token, pair_of;
   uint64_t h, y, h_shared, y_shared;
+  uint64_t prep, prep_bytes;  // prepared activations of the K-sliced stages (0 bytes: unused)
   uint64_t total;
 };
+
+// Whether the routed stages of a call with this many pairs over this many
+// expert slots take the K-sliced matrix-core stage (and its prepared
+// activations), and the bytes those need for V vectors of cols values.
+bool gmk_wanted(int pairs, int slots);
+uint64_t gmk_prep_bytes(uint64_t V, int cols);
 
 struct LayerInfo {
   smoe_layer_desc desc;
@@ -88,15 +95,17 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int3
 
 // pairs: routed (token, expert) pairs of the call (T for the shared expert),
 // used to size the launch.
+// prep: workspace for prepared activations (gmk_prep_bytes of the stage), or
+// null when the call has none.
 hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xmode,
                           float rms_eps, int T, int pairs, int max_slots, const int* meta,
                           const int* active, const int* offs, const int* pair_token,
-                          float* h, hipStream_t stream);
+                          float* h, hipStream_t stream, void* prep);
 
 hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int pairs,
                        int max_slots,
                        const int* meta, const int* active, const int* offs, float* y,
-                       hipStream_t stream);
+                       hipStream_t stream, void* prep);
 
 // Batch-1 path (two launches); sets *launched = false (and enqueues nothing)
 // when the layer's shape has no instantiation.

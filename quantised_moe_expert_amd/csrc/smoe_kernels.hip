@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "smoe_gemv.hpp"
 #include "smoe_gemv_args.hpp"
 #include "smoe_internal.hpp"
 
@@ -462,10 +463,128 @@ static hipError_t gm_dispatch(int bits, const GemvArgs& A, bool gate_up, int in,
                    : launch_gm<2, ST>(A, gate_up, in, nw, grid, lds, s);
 }
 
+// Slots averaging this many routed pairs or more take the K-sliced stage
+// (64 tokens per weight read) instead of 16-token chunks.
+#ifndef SMOE_GMK_MIN_MEAN
+#define SMOE_GMK_MIN_MEAN 24
+#endif
+
+bool gmk_wanted(int pairs, int slots) {
+  return slots > 0 && pairs / slots >= SMOE_GMK_MIN_MEAN;
+}
+
+static uint64_t al256(uint64_t v) { return (v + 255) / 256 * 256; }
+
+uint64_t gmk_prep_bytes(uint64_t V, int cols) {
+  return al256(V * (uint64_t)cols * 2) + al256(V * (uint64_t)(cols / 64) * 4) + al256(V * 4);
+}
+
+// Activation vectors for the K-sliced stage, one workgroup per vector v: the
+// power-of-two scale S that puts the largest magnitude just below 2^14, the
+// fp16 pairs of every code word pre-divided by 2^p in the order of the MFMA
+// operand (word cw, half hv -> quad cw * (PPW / 4) + hv of 16 bytes), the
+// offset K = sum of the pairs times (1024 + m 2^p) of every scale group, and
+// the output factor rms / (m S). The same arithmetic as k_gemm's staging.
+template <int BITS, bool XF32>
+__global__ __launch_bounds__(256) void k_gmk_prep(const void* x, int ld, int cols, int rms,
+                                                  float eps, uint32_t* xq, float* xk, float* xo) {
+  constexpr int WPW = QT<BITS>::WPW, PPW = QT<BITS>::PPW, NPOS = QT<BITS>::NPOS;
+  constexpr int WPG = QT<BITS>::WPG, HALVES = PPW / 4;
+  __shared__ float s_r[4][2];
+  const int v = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const void* row = (const uint8_t*)x + (size_t)v * ld * (XF32 ? 4 : 2);
+  const int Wr = cols / WPW, G = cols / 64;
+  float amax = 0.f, ss = 0.f;
+  for (int cw = tid; cw < Wr; cw += 256) {
+    float xv[WPW];
+    gv_load_word<BITS, XF32>(row, cw, xv);
+#pragma unroll
+    for (int j = 0; j < WPW; ++j) {
+      amax = fmaxf(amax, fabsf(xv[j]));
+      ss = fmaf(xv[j], xv[j], ss);
+    }
+  }
+  amax = lane63(seg_max(amax, 6));
+  ss = lane63(seg_sum(ss, 6));
+  if (lane == 0) {
+    s_r[wave][0] = amax;
+    s_r[wave][1] = ss;
+  }
+  __syncthreads();
+  float m = 0.f, q2 = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    m = fmaxf(m, s_r[w][0]);
+    q2 += s_r[w][1];
+  }
+  int ex = 0;
+  frexpf(m, &ex);
+  ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+  const float S = ldexpf(1.0f, 14 - ex);
+  if (tid == 0) {
+    const float rr = rms ? 1.0f / sqrtf(q2 / (float)cols + eps) : 1.0f;
+    xo[v] = rr / (QT<BITS>::M * S);
+  }
+  uint32_t* q = xq + (size_t)v * (cols / 2);
+  for (int g = tid; g < G; g += 256) {
+    float kk = 0.f;
+    for (int j = 0; j < WPG; ++j) {
+      const int cw = g * WPG + j;
+      float xv[WPW];
+      gv_load_word<BITS, XF32>(row, cw, xv);
+#pragma unroll
+      for (int p = 0; p < PPW; ++p) {
+        const int hs = p / NPOS, pos = p % NPOS;
+        const int ia = hs * NPOS + pos, ib = ia + WPW / 2;
+        const float f = S * (1.0f / (float)(1 << (BITS * pos)));
+        const _Float16 ha = (_Float16)(xv[ia] * f), hb = (_Float16)(xv[ib] * f);
+        q[(cw * HALVES + p / 4) * 4 + p % 4] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
+        kk = fmaf((float)ha + (float)hb, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)), kk);
+      }
+    }
+    xk[(size_t)v * G + g] = kk;
+  }
+}
+
+static hipError_t gmk_dispatch(const LayerInfo& L, GemvArgs& A, bool gate_up, const void* x,
+                               bool xf32, int V, int rows, int cols, int slots, void* prep,
+                               hipStream_t s) {
+  uint8_t* base = (uint8_t*)prep;
+  uint32_t* xq = (uint32_t*)base;
+  float* xk = (float*)(base + al256((uint64_t)V * cols * 2));
+  float* xo = (float*)(base + al256((uint64_t)V * cols * 2) + al256((uint64_t)V * (cols / 64) * 4));
+  A.prep_x = xq;
+  A.prep_k = xk;
+  A.prep_o = xo;
+  if (V > 0) {
+    const dim3 pg(V), pb(256);
+    if (L.desc.bits == 4) {
+      if (xf32)
+        hipLaunchKernelGGL((k_gmk_prep<4, true>), pg, pb, 0, s, x, cols, cols, A.rms, A.eps, xq, xk, xo);
+      else
+        hipLaunchKernelGGL((k_gmk_prep<4, false>), pg, pb, 0, s, x, cols, cols, A.rms, A.eps, xq, xk, xo);
+    } else {
+      if (xf32)
+        hipLaunchKernelGGL((k_gmk_prep<2, true>), pg, pb, 0, s, x, cols, cols, A.rms, A.eps, xq, xk, xo);
+      else
+        hipLaunchKernelGGL((k_gmk_prep<2, false>), pg, pb, 0, s, x, cols, cols, A.rms, A.eps, xq, xk, xo);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int rpb = gmk_rows_per_block(gate_up, cols / 64 % 4 == 0);
+  const dim3 grid((rows + rpb - 1) / rpb, slots);
+  if (L.desc.bits == 4)
+    return L.desc.scale_dtype == SMOE_SCALE_F32 ? launch_gm_ks<4, float>(A, gate_up, grid, s)
+                                                : launch_gm_ks<4, _Float16>(A, gate_up, grid, s);
+  return L.desc.scale_dtype == SMOE_SCALE_F32 ? launch_gm_ks<2, float>(A, gate_up, grid, s)
+                                              : launch_gm_ks<2, _Float16>(A, gate_up, grid, s);
+}
+
 hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xmode,
                           float rms_eps, int T, int pairs, int max_slots, const int* meta,
                           const int* active, const int* offs, const int* pair_token,
-                          float* h, hipStream_t stream) {
+                          float* h, hipStream_t stream, void* prep) {
   const ExpertPlan& P = shared ? L.shared_plan : L.plan;
   GemvArgs A{};
   A.blobs = shared ? L.shared : L.blobs;
@@ -485,6 +604,8 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
   A.pair_token = pair_token;
   A.out = h;
   const int in = xmode == X_BF16 ? GV_BF16 : GV_F32_SPLIT;
+  if (prep && !shared && in == GV_BF16 && gmk_wanted(pairs, max_slots))
+    return gmk_dispatch(L, A, true, x, false, T, P.gate.rows, P.d_model, max_slots, prep, stream);
   dim3 grid;
   unsigned lds;
   int nw;
@@ -506,7 +627,7 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
 hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int pairs,
                        int max_slots,
                        const int* meta, const int* active, const int* offs, float* y,
-                       hipStream_t stream) {
+                       hipStream_t stream, void* prep) {
   const ExpertPlan& P = shared ? L.shared_plan : L.plan;
   GemvArgs A{};
   A.blobs = shared ? L.shared : L.blobs;
@@ -522,6 +643,8 @@ hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, i
   A.active = active;
   A.offs = offs;
   A.out = y;
+  if (prep && !shared && gmk_wanted(pairs, max_slots))
+    return gmk_dispatch(L, A, false, h, true, pairs, P.down.rows, P.ffn, max_slots, prep, stream);
   dim3 grid;
   unsigned lds;
   int nw;

@@ -296,6 +296,22 @@ def test_prefill_sized_batch_eight_wave_chunks(x_dtype):
     _check_layer(hl, x, lg, 2, True, x_dtype)
 
 
+@pytest.mark.parametrize("bits,sd,d,ffn", [(2, "f16", 640, 192), (4, "f16", 576, 320),
+                                           (4, "f32", 1024, 512)])
+def test_k_sliced_stage_many_tokens_per_expert(bits, sd, d, ffn):
+    """Slots of 64 tokens and more (several 64-token chunks per slot, ragged
+    last chunks), K slices with a partial last slice, rows that are not a
+    multiple of the 64/128-row blocks, scale groups per row not a multiple
+    of four (scalar scale loads)."""
+    _torch()
+    hl = random_layer(4300 + bits + d, d, ffn, 4, bits, sd)
+    r = synth.rng(4301 + d)
+    T = 300
+    x = _x(r, T, d, "bf16")
+    lg = synth.normal_f32(r, (T, 4))
+    _check_layer(hl, x, lg, 2, True, "bf16")
+
+
 def test_qwen235b_q4_t512_sampled():
     _torch()
     W = synth.WORKLOADS["qwen235b_q4_t512"]
