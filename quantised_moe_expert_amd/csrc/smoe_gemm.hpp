@@ -581,7 +581,7 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
     u32x4 sq[TPW];
     float s[TPW][SV ? 1 : GB];
   };
-  auto load = [&](Batch& B, int sl) {  // slice sl (clamped) of this lane's rows
+  auto load = [&](Batch& B, int sl) __attribute__((always_inline)) {  // slice sl (clamped) of this lane's rows
     const int g0 = min(sl, NSL - 1) * KSG;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
     }
   };
   // SV: quarters 0 and 2 loaded quad 0 of the slice, 1 and 3 quad 1
-  auto scales = [&](const Batch& B, int t, float* sc) {
+  auto scales = [&](const Batch& B, int t, float* sc) __attribute__((always_inline)) {
     if constexpr (SV) {
       uint32_t q[4] = {B.sq[t].x, B.sq[t].y, B.sq[t].z, B.sq[t].w};
 #pragma unroll
@@ -623,7 +623,7 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
   // tokens of slice sl (clamped) into buffer buf: wave w copies quads
   // w * 8 .. w * 8 + 7 of the slice for all 64 tokens, and the offsets of
   // group w
-  auto stage = [&](int v, int sl, int buf) {
+  auto stage = [&](int v, int sl, int buf) __attribute__((always_inline)) {
     const int s = min(sl, NSL - 1);
     const u32x4* src = xq + (size_t)v * (cols / 8) + (size_t)s * QPS;
 #pragma unroll
@@ -645,7 +645,10 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
   };
 
   f32x4m acc[TPW][NTT];
-  auto compute = [&](const Batch& B, int sl, int buf) {
+  // NA: token tiles multiplied (all four; a separate two-tile path for
+  // half-empty chunks measured slower: its registers spilled)
+  auto compute = [&](const Batch& B, int sl, int buf, auto na) __attribute__((always_inline)) {
+    constexpr int NA = decltype(na)::value;
     const int g0 = sl * KSG;
     const int glast = min(G - 1 - g0, KSG - 1);
     uint32_t w[TPW][NU][4];
@@ -669,10 +672,13 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
         for (int u = 0; u < TPW; ++u)
           op[h][u] = gm_operand<BITS>(word(w[u], j, BITS == 4 ? h : 0), BITS == 4 ? 0 : h, magic);
 #pragma unroll
-      for (int t = 0; t < NTT; ++t) {
+      for (int t = 0; t < NA; ++t) {
+        // the MFMAs start from -K, so they leave D - K (the offsets of the
+        // fp16 pairs and the code midpoint removed) in one chain
+        const f32x4m nk = *(const f32x4m*)(Kb + gl * TC + 16 * t + 4 * b);
         f32x4m d[TPW];
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) d[u] = f32x4m{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < TPW; ++u) d[u] = nk;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int hv = BITS == 4 ? 0 : h;
@@ -682,16 +688,14 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
           for (int u = 0; u < TPW; ++u)
             d[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, op[h][u], d[u], 0, 0, 0);
         }
-        const f32x4m kv = *(const f32x4m*)(Kb + gl * TC + 16 * t + 4 * b);
-        const float k0 = kv.x, k1 = kv.y, k2 = kv.z, k3 = kv.w;
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
           const float sj = own ? sc[u][j] : 0.f;
           const float a0 = d[u].x, a1 = d[u].y, a2 = d[u].z, a3 = d[u].w;
-          acc[u][t].x = fmaf(sj, a0 - k0, acc[u][t].x);
-          acc[u][t].y = fmaf(sj, a1 - k1, acc[u][t].y);
-          acc[u][t].z = fmaf(sj, a2 - k2, acc[u][t].z);
-          acc[u][t].w = fmaf(sj, a3 - k3, acc[u][t].w);
+          acc[u][t].x = fmaf(sj, a0, acc[u][t].x);
+          acc[u][t].y = fmaf(sj, a1, acc[u][t].y);
+          acc[u][t].z = fmaf(sj, a2, acc[u][t].z);
+          acc[u][t].w = fmaf(sj, a3, acc[u][t].w);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -716,21 +720,24 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
     __syncthreads();
     // slices in pairs; every load of the next slice is issued before the
     // current one is multiplied, and complete before the barrier
-    for (int sl = 0; sl < NSL; sl += 2) {
-      load(bB, sl + 1);
-      stage(v, sl + 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(bA, sl, 0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (sl + 1 >= NSL) break;
-      load(bA, sl + 2);
-      stage(v, sl + 2, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(bB, sl + 1, 1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
+    auto slices = [&](auto na) __attribute__((always_inline)) {
+      for (int sl = 0; sl < NSL; sl += 2) {
+        load(bB, sl + 1);
+        stage(v, sl + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(bA, sl, 0, na);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (sl + 1 >= NSL) break;
+        load(bA, sl + 2);
+        stage(v, sl + 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(bB, sl + 1, 1, na);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    };
+    slices(std::integral_constant<int, NTT>{});
     // outputs: lane (r, b) holds tokens 16t + 4b .. + 3 of its rows
     if constexpr (GU) {
       // the up waves hand their sums to the gate waves of the same tiles

@@ -483,8 +483,9 @@ uint64_t gmk_prep_bytes(uint64_t V, int cols) {
 // power-of-two scale S that puts the largest magnitude just below 2^14, the
 // fp16 pairs of every code word pre-divided by 2^p in the order of the MFMA
 // operand (word cw, half hv -> quad cw * (PPW / 4) + hv of 16 bytes), the
-// offset K = sum of the pairs times (1024 + m 2^p) of every scale group, and
-// the output factor rms / (m S). The same arithmetic as k_gemm's staging.
+// offset K = sum of the pairs times (1024 + m 2^p) of every scale group
+// (stored as -K), and the output factor rms / (m S). The same arithmetic as
+// k_gemm's staging.
 template <int BITS, bool XF32>
 __global__ __launch_bounds__(256) void k_gmk_prep(const void* x, int ld, int cols, int rms,
                                                   float eps, uint32_t* xq, float* xk, float* xo) {
@@ -542,7 +543,7 @@ __global__ __launch_bounds__(256) void k_gmk_prep(const void* x, int ld, int col
         kk = fmaf((float)ha + (float)hb, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)), kk);
       }
     }
-    xk[(size_t)v * G + g] = kk;
+    xk[(size_t)v * G + g] = -kk;  // stored negated: the MFMA chains start from it
   }
 }
 
