@@ -215,10 +215,10 @@ int smoe_route_ex(const float* d_logits, int n_tokens, int n_experts, int top_k,
  *  d_workspace at least smoe_workspace_bytes(layer, n_tokens, top_k) bytes,
  *             256-byte aligned; contents are scratch and need no clearing.
  * Tokens that share an expert read its weights once per call.
- * Errors: SMOE_E_ARG, SMOE_E_WORKSPACE, SMOE_E_UNSUPPORTED (the per-expert
- * token bitmasks of the grouping, num_experts * ceil(n_tokens / 32) * 4 +
- * num_experts * 8 bytes, exceed 160 KB: e.g. more than ~2400 tokens with 512
- * experts), SMOE_E_HIP. n_tokens == 0 is a no-op.
+ * Errors: SMOE_E_ARG, SMOE_E_WORKSPACE, SMOE_E_UNSUPPORTED (the grouping's
+ * per-expert token bitmasks and counts, (num_experts * (w + ceil(w / 8) + 3)
+ * + 1) * 4 bytes with w = ceil(n_tokens / 32), exceed 160 KB: e.g. more than
+ * ~2150 tokens with 512 experts), SMOE_E_HIP. n_tokens == 0 is a no-op.
  * Activations must be finite with |x| < 2^100 (they are rescaled by a power
  * of two per vector before the fp16 dot products). */
 int smoe_moe_forward(const smoe_layer* layer, const void* d_x, int x_dtype,

@@ -68,11 +68,14 @@ enum XMode : int {
   X_F32_RMS = 2,    // fp32 residual stream; the stage applies unit-gain RMSNorm
 };
 
-// Grouping (T > 1) keeps a token bitmask per expert in LDS: E * ceil(T / 32)
-// words plus 2 E, at most 160 KB.
-inline bool group_fits(int E, int T) {
-  return (int64_t)E * ((T + 31) / 32) * 4 + (int64_t)E * 8 <= 160 * 1024;
+// Grouping (T > 1) keeps in LDS a token bitmask per expert (E * ceil(T / 32)
+// words), the token counts before every eighth word of it (E * ceil(T / 256)
+// words) and 3 E + 1 words of slot bookkeeping; at most 160 KB.
+inline int64_t group_lds_bytes(int E, int T) {
+  const int64_t tw = (T + 31) / 32, tw8 = (tw + 7) / 8;
+  return ((int64_t)E * (tw + tw8 + 3) + 1) * 4;
 }
+inline bool group_fits(int E, int T) { return group_lds_bytes(E, T) <= 160 * 1024; }
 
 // Routing variants, as the kernels take them (the ABI's smoe_route_opts
 // after validation). Default-constructed = plain softmax routing.

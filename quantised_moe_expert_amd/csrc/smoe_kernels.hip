@@ -214,10 +214,12 @@ constexpr int GROUP_THREADS = 1024;
 
 __global__ __launch_bounds__(GROUP_THREADS) void k_group(RouteArgs A) {
   extern __shared__ uint32_t lds[];
-  const int TW = (A.T + 31) >> 5;
+  const int TW = (A.T + 31) >> 5, TW8 = (TW + 7) >> 3;
   uint32_t* sel = lds;                          // [E][TW] token bitmask per expert
-  int* slot_of = (int*)(lds + A.E * TW);        // [E]
+  int* pre8 = (int*)(sel + A.E * TW);           // [E][TW8] tokens before every 8th word
+  int* slot_of = pre8 + A.E * TW8;              // [E]
   int* cnt = slot_of + A.E;                     // [E]
+  int* offs = cnt + A.E;                        // [E + 1] (slot order)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = A.T * A.k;
   for (int i = tid; i < A.E * TW; i += blockDim.x) sel[i] = 0u;
@@ -227,9 +229,22 @@ __global__ __launch_bounds__(GROUP_THREADS) void k_group(RouteArgs A) {
     atomicOr(&sel[A.ids[i] * TW + (t >> 5)], 1u << (t & 31));
   }
   __syncthreads();
+  // per expert and block of eight words: tokens before the block (threads
+  // take (expert, block) pairs; each expert's blocks are then summed up)
+  for (int u = tid; u < A.E * TW8; u += blockDim.x) {
+    const int e = u / TW8, q8 = u - e * TW8;
+    int c = 0;
+    for (int q = q8 * 8; q < min(q8 * 8 + 8, TW); ++q) c += __popc(sel[e * TW + q]);
+    pre8[u] = c;
+  }
+  __syncthreads();
   for (int e = tid; e < A.E; e += blockDim.x) {
     int c = 0;
-    for (int i = 0; i < TW; ++i) c += __popc(sel[e * TW + i]);
+    for (int q8 = 0; q8 < TW8; ++q8) {
+      const int b = pre8[e * TW8 + q8];
+      pre8[e * TW8 + q8] = c;
+      c += b;
+    }
     cnt[e] = c;
   }
   __syncthreads();
@@ -251,6 +266,7 @@ __global__ __launch_bounds__(GROUP_THREADS) void k_group(RouteArgs A) {
       if (act) {
         const int s = nact + ia - 1;
         slot_of[e] = s;
+        offs[s] = npairs + ic - c;
         A.active[s] = e;
         A.offs[s] = npairs + ic - c;
       }
@@ -264,14 +280,18 @@ __global__ __launch_bounds__(GROUP_THREADS) void k_group(RouteArgs A) {
     }
   }
   __syncthreads();
+  // pair (t, j): its rank among the expert's tokens is the tokens before its
+  // word's block, plus the words of the block before its word, plus the bits
+  // below it in its word
   for (int i = tid; i < P; i += blockDim.x) {
     const int t = i / A.k;
     const int e = A.ids[i];
     const uint32_t* row = sel + e * TW;
-    int rank = 0;
-    for (int q = 0; q < (t >> 5); ++q) rank += __popc(row[q]);
-    rank += __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
-    const int pos = A.offs[slot_of[e]] + rank;
+    const int q = t >> 5;
+    int rank = pre8[e * TW8 + (q >> 3)];
+    for (int qq = q & ~7; qq < q; ++qq) rank += __popc(row[qq]);
+    rank += __popc(row[q] & ((1u << (t & 31)) - 1u));
+    const int pos = offs[slot_of[e]] + rank;
     A.pair_token[pos] = t;
     A.pair_of[i] = pos;
   }
@@ -296,8 +316,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int3
   else
     hipLaunchKernelGGL(k_topk<8>, grid, block, 0, stream, A);
   if (!group) return hipGetLastError();
-  const int TW = (T + 31) / 32;
-  const size_t lds = (size_t)E * TW * 4 + (size_t)E * 8;
+  const size_t lds = group_lds_bytes(E, T);
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute((const void*)k_group,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
