@@ -517,8 +517,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemvArgs A) {
 //     fp16 pairs, group offsets K and output factors of k_gemm's staging,
 //     stored per vector in the order of the MFMA operand, so a slice is
 //     copied global -> LDS with direct-to-LDS loads (global_load_lds_dwordx4:
-//     lane i writes 16 bytes at LDS base + 16 i; lane = token), no
-//     registers and no conversion in this kernel.
+//     lane i writes 16 bytes at LDS base + 16 i), no registers and no
+//     conversion in this kernel. One load moves one token's slice (a
+//     contiguous kilobyte, 8 cache lines); token rows in LDS are one quad
+//     longer than the slice, so the 16 tokens an MFMA operand read touches
+//     sit on distinct banks.
 //   - Each wave owns one 16-row tile of one matrix: for gate/up, waves 0-3
 //     take four gate tiles and waves 4-7 the up tiles of the same 64 rows
 //     (their results meet in LDS for SwiGLU); for down, eight tiles.
@@ -536,7 +539,8 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
   static_assert(TC == 64, "one direct-to-LDS load per token per lane");
   constexpr int QPS = KSG * WPG * HALVES;  // 16-byte pair quads of a slice per token
   static_assert(QPS == 64, "a slice is 512 weights");
-  constexpr int XB = QPS * TC * 4, KB = KSG * TC;
+  static_assert(GMK_XTS == (QPS + 1) * 4, "token rows of one slice and a padding quad");
+  constexpr int XB = TC * GMK_XTS, KB = KSG * TC;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slot = blockIdx.y;
@@ -620,21 +624,21 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
     const int p = pc + min(lane, nt - 1);
     return GU ? A.pair_token[p] : p;
   };
-  // tokens of slice sl (clamped) into buffer buf: wave w copies quads
-  // w * 8 .. w * 8 + 7 of the slice for all 64 tokens, and the offsets of
-  // group w
+  // tokens of slice sl (clamped) into buffer buf: wave w copies the slices
+  // of tokens w * 8 .. w * 8 + 7, one contiguous kilobyte per load (lane i
+  // quad i), and the offsets of group w for all 64 tokens
   auto stage = [&](int v, int sl, int buf) __attribute__((always_inline)) {
     const int s = min(sl, NSL - 1);
-    const u32x4* src = xq + (size_t)v * (cols / 8) + (size_t)s * QPS;
+    // a slice past the row's end (G not a multiple of 8) re-reads the row's
+    // last quad; those entries are never used
+    const int qc = min(s * QPS + lane, cols / 8 - 1);
 #pragma unroll
-    for (int i = 0; i < QPS / GMK_NW; ++i) {
-      const int qd = wave * (QPS / GMK_NW) + i;
-      // a slice past the row's end (G not a multiple of 8) re-reads the
-      // row's last quads; those entries are never used
-      const int qc = min(s * QPS + qd, cols / 8 - 1) - s * QPS;
-      __builtin_amdgcn_global_load_lds((const void*)(src + qc),
+    for (int i = 0; i < TC / GMK_NW; ++i) {
+      const int tk = wave * (TC / GMK_NW) + i;
+      const int vt = __builtin_amdgcn_readlane(v, tk);
+      __builtin_amdgcn_global_load_lds((const void*)(xq + (size_t)vt * (cols / 8) + qc),
                                        (__attribute__((address_space(3))) void*)(X + buf * XB +
-                                                                                 qd * TC * 4),
+                                                                                 tk * GMK_XTS),
                                        16, 0, 0);
     }
     const int g = min(s * KSG + wave, G - 1);
@@ -683,7 +687,7 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
         for (int h = 0; h < 2; ++h) {
           const int hv = BITS == 4 ? 0 : h;
           const int qd = BITS == 4 ? (gl * WPG + wmap + h) : (gl * WPG + wmap) * HALVES + hv;
-          const h8 av = __builtin_bit_cast(h8, *(const u32x4*)(Xb + (qd * TC + 16 * t + r) * 4));
+          const h8 av = __builtin_bit_cast(h8, *(const u32x4*)(Xb + (16 * t + r) * GMK_XTS + qd * 4));
 #pragma unroll
           for (int u = 0; u < TPW; ++u)
             d[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, op[h][u], d[u], 0, 0, 0);
@@ -698,7 +702,6 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
           acc[u][t].w = fmaf(sj, a3, acc[u][t].w);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 

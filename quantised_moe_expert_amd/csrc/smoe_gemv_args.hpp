@@ -72,14 +72,18 @@ __host__ __device__ constexpr int gmk_rows_per_block(bool gate_up, bool sv) {
   return (gate_up ? 4 : GMK_NW) * gmk_tpw(sv) * 16;
 }
 
+// a token's slice in LDS: KSG * 8 pair quads and one quad of padding, so
+// that the rows of 16 consecutive tokens start on 16 different bank quads
+constexpr int GMK_XTS = (GMK_KSG * 8 + 1) * 4;  // 32-bit words per token row
+
 struct GmkLds {
   int x, k, s, osc, total;  // offsets and size in 32-bit words
 };
 
 __host__ __device__ inline GmkLds gmk_lds_layout() {
   GmkLds L;
-  L.x = 0;                                     // 2 buffers of KSG * 32 * TC pairs
-  L.k = L.x + 2 * GMK_KSG * 32 * GMK_TC;       // 2 buffers of KSG * TC offsets
+  L.x = 0;                                     // 2 buffers of TC token rows
+  L.k = L.x + 2 * GMK_TC * GMK_XTS;            // 2 buffers of KSG * TC offsets
   L.s = L.k + 2 * GMK_KSG * GMK_TC;            // per-token power-of-two scale
   L.osc = L.s + GMK_TC;                        // per-token output factor
   L.total = L.osc + GMK_TC;
