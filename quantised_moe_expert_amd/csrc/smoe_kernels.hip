@@ -329,35 +329,58 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int3
 // ---------------------------------------------------------------- combine --
 // out[t, i] (+)= sum_j w[t, j] * y[pair_of[t, j], i] + y_shared[t, i]
 
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
-                                                 const int* __restrict__ pair_of,
-                                                 const float* __restrict__ w,
-                                                 const float* __restrict__ y_shared,
-                                                 const float* __restrict__ shared_gate,
-                                                 float* __restrict__ out, int k, int d,
-                                                 int accumulate) {
+constexpr int COMBINE_THREADS = 128;
+
+// VEC consecutive outputs per thread (4: 16-byte loads and stores, when out
+// is 16-byte aligned); the sum order over j is the same for both widths
+template <int VEC>
+__global__ __launch_bounds__(COMBINE_THREADS) void k_combine(const float* __restrict__ y,
+                                                             const int* __restrict__ pair_of,
+                                                             const float* __restrict__ w,
+                                                             const float* __restrict__ y_shared,
+                                                             const float* __restrict__ shared_gate,
+                                                             float* __restrict__ out, int k, int d,
+                                                             int accumulate) {
+  using V = float __attribute__((ext_vector_type(VEC)));
   const int t = blockIdx.y;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = (blockIdx.x * COMBINE_THREADS + threadIdx.x) * VEC;
   if (i >= d) return;
-  float acc = 0.f;
+  V acc = {};
   for (int j = 0; j < k; ++j) {
     const int o = t * k + j;
-    acc = fmaf(w[o], y[(size_t)pair_of[o] * d + i], acc);
+    const V yv = *(const V*)(y + (size_t)pair_of[o] * d + i);
+    const float wj = w[o];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] = fmaf(wj, yv[c], acc[c]);
   }
   if (y_shared) {
-    const float ys = y_shared[(size_t)t * d + i];
-    acc += shared_gate ? ys / (1.0f + expf(-shared_gate[t])) : ys;
+    const V ys = *(const V*)(y_shared + (size_t)t * d + i);
+    const float den = shared_gate ? 1.0f + expf(-shared_gate[t]) : 1.0f;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] += shared_gate ? ys[c] / den : ys[c];
   }
-  float* dst = out + (size_t)t * d + i;
-  *dst = accumulate ? *dst + acc : acc;
+  V* dst = (V*)(out + (size_t)t * d + i);
+  if (accumulate) {
+    const V o = *dst;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] = o[c] + acc[c];
+  }
+  *dst = acc;
 }
 
 hipError_t launch_combine(const float* y, const int* pair_of, const float* w,
                           const float* y_shared, const float* shared_gate, float* out, int T,
                           int k, int d, int accumulate, hipStream_t stream) {
-  dim3 grid((d + 255) / 256, T);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, stream, y, pair_of, w, y_shared, shared_gate,
-                     out, k, d, accumulate);
+  // y and y_shared are workspace rows (256-byte aligned, d a multiple of 64)
+  if (((uintptr_t)out & 15) == 0 && d % 4 == 0) {
+    dim3 grid((d + 4 * COMBINE_THREADS - 1) / (4 * COMBINE_THREADS), T);
+    hipLaunchKernelGGL(k_combine<4>, grid, dim3(COMBINE_THREADS), 0, stream, y, pair_of, w,
+                       y_shared, shared_gate, out, k, d, accumulate);
+  } else {
+    dim3 grid((d + COMBINE_THREADS - 1) / COMBINE_THREADS, T);
+    hipLaunchKernelGGL(k_combine<1>, grid, dim3(COMBINE_THREADS), 0, stream, y, pair_of, w,
+                       y_shared, shared_gate, out, k, d, accumulate);
+  }
   return hipGetLastError();
 }
 
@@ -545,24 +568,37 @@ __global__ __launch_bounds__(256) void k_gmk_prep(const void* x, int ld, int col
     const float rr = rms ? 1.0f / sqrtf(q2 / (float)cols + eps) : 1.0f;
     xo[v] = rr / (QT<BITS>::M * S);
   }
+  // one code word per thread: its fp16 pairs leave as 16-byte stores, and
+  // the group offset K is summed over the WPG consecutive lanes that hold
+  // the group (Wr and 256 are multiples of WPG, so a lane segment is either
+  // wholly inside the row or wholly past it)
+  constexpr int LGW = WPG == 8 ? 3 : 2;
+  static_assert((1 << LGW) == WPG, "words per group");
   uint32_t* q = xq + (size_t)v * (cols / 2);
-  for (int g = tid; g < G; g += 256) {
+  for (int c0 = 0; c0 < Wr; c0 += 256) {
+    const int cw = c0 + tid;
     float kk = 0.f;
-    for (int j = 0; j < WPG; ++j) {
-      const int cw = g * WPG + j;
+    if (cw < Wr) {
       float xv[WPW];
       gv_load_word<BITS, XF32>(row, cw, xv);
+      uint32_t pr[PPW];
 #pragma unroll
       for (int p = 0; p < PPW; ++p) {
         const int hs = p / NPOS, pos = p % NPOS;
         const int ia = hs * NPOS + pos, ib = ia + WPW / 2;
         const float f = S * (1.0f / (float)(1 << (BITS * pos)));
         const _Float16 ha = (_Float16)(xv[ia] * f), hb = (_Float16)(xv[ib] * f);
-        q[(cw * HALVES + p / 4) * 4 + p % 4] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
+        pr[p] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
         kk = fmaf((float)ha + (float)hb, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)), kk);
       }
+#pragma unroll
+      for (int hq = 0; hq < HALVES; ++hq)
+        *(u32x4*)(q + (cw * HALVES + hq) * 4) =
+            u32x4{pr[4 * hq], pr[4 * hq + 1], pr[4 * hq + 2], pr[4 * hq + 3]};
     }
-    xk[(size_t)v * G + g] = -kk;  // stored negated: the MFMA chains start from it
+    kk = seg_sum(kk, LGW);
+    // stored negated: the MFMA chains start from it
+    if (cw < Wr && (cw & (WPG - 1)) == WPG - 1) xk[(size_t)v * G + cw / WPG] = -kk;
   }
 }
 
