@@ -543,7 +543,19 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
   constexpr int XB = TC * GMK_XTS, KB = KSG * TC;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int slot = blockIdx.y;
+  // workgroup L of the launch runs on XCD L % 8 (round-robin dispatch); give
+  // each XCD whole slots, so the row blocks that share a slot's token slices
+  // share that XCD's L2 (the slots past the last multiple of 8 keep the
+  // plain order)
+  int bx = blockIdx.x, slot = blockIdx.y;
+  {
+    const int nbx = gridDim.x, L = bx + slot * nbx;
+    if (L < (int)(gridDim.y & ~7u) * nbx) {
+      const int q = L >> 3;
+      slot = q / nbx * 8 + (L & 7);
+      bx = q % nbx;
+    }
+  }
   if (slot >= A.meta[0]) return;  // workgroup-uniform
   const int e = A.active[slot], p0 = A.offs[slot], p1 = A.offs[slot + 1];
   if (p0 >= p1) return;
@@ -559,7 +571,7 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
   const ST* sw0[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    row[u] = ((blockIdx.x * (GU ? 4 : GMK_NW) + tw) * TPW + u) * 16 + r;
+    row[u] = ((bx * (GU ? 4 : GMK_NW) + tw) * TPW + u) * 16 + r;
     const int rc = min(row[u], rows - 1);
     cw0[u] = (const uint32_t*)(blob + M.codes_off) + (size_t)rc * Wr;
     sw0[u] = (const ST*)(blob + M.scales_off) + (size_t)rc * G;
