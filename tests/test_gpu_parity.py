@@ -312,6 +312,19 @@ def test_k_sliced_stage_many_tokens_per_expert(bits, sd, d, ffn):
     _check_layer(hl, x, lg, 2, True, "bf16")
 
 
+@pytest.mark.parametrize("E,T,d,ffn,sd", [(12, 400, 512, 256, "f32"), (20, 640, 576, 320, "f16")])
+def test_k_sliced_stage_xcd_order_with_remainder_slots(E, T, d, ffn, sd):
+    """Eight or more slots: the K-sliced stage hands each XCD whole slots
+    (the first multiple of eight) and keeps the plain order for the rest;
+    every token of every slot is checked."""
+    _torch()
+    hl = random_layer(4400 + E, d, ffn, E, 4, sd)
+    r = synth.rng(4401 + E)
+    x = _x(r, T, d, "bf16")
+    lg = synth.normal_f32(r, (T, E))
+    _check_layer(hl, x, lg, 2, True, "bf16")
+
+
 def test_qwen235b_q4_t512_sampled():
     _torch()
     W = synth.WORKLOADS["qwen235b_q4_t512"]
