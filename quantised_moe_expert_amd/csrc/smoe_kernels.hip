@@ -466,6 +466,11 @@ static void grouped_shape(const MatPlan& m, bool split, int slots, GemvArgs& A, 
 #ifndef SMOE_GM_TC_MIN
 #define SMOE_GM_TC_MIN 8
 #endif
+// (512 measured best against 256, 384, 1024 and 3000 on the 8- and 32-token
+// layers: fewer, longer workgroups while two rounds still fill the GPU)
+#ifndef SMOE_GM_MIN_WG
+#define SMOE_GM_MIN_WG 512
+#endif
 static bool gm_shape(const MatPlan& m, bool split, int pairs, int slots, GemvArgs& A, dim3& grid,
                      unsigned& lds, int& nw) {
   const int tiles = (m.rows + 15) / 16;
@@ -480,12 +485,12 @@ static bool gm_shape(const MatPlan& m, bool split, int pairs, int slots, GemvArg
   const int ks = nw == 4 && (int64_t)(tiles + nw - 1) / nw * slots < 1024 ? nw : 1;
   A.ksplit = ks;
   const int tpb = nw / ks;
-  // tiles per wave: more while the grid keeps over 1024 workgroups, so that
-  // each staging of the tokens serves more rows
+  // tiles per wave: more while the grid keeps over SMOE_GM_MIN_WG
+  // workgroups, so that each staging of the tokens serves more rows
   int tpw = 1;
   if (ks == 1)
     while (tpw < SMOE_GM_TPW_MAX &&
-           (int64_t)((tiles + tpb * 2 * tpw - 1) / (tpb * 2 * tpw)) * slots >= 1024)
+           (int64_t)((tiles + tpb * 2 * tpw - 1) / (tpb * 2 * tpw)) * slots >= SMOE_GM_MIN_WG)
       tpw *= 2;
   A.tiles_per_wave = tpw;
   grid = dim3((tiles + tpb * tpw - 1) / (tpb * tpw), slots);
