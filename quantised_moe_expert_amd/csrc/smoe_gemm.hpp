@@ -229,8 +229,10 @@ __device__ __forceinline__ void gm_unit_arrange(const u32x4& t, uint32_t w[4]) {
   }
 }
 
+// Q2 down with 4 waves: asking for 4 waves per SIMD keeps the kernel in 128
+// registers (it took 132, three waves); the others are left to the compiler
 template <int BITS, typename ST, int IN, bool GU, bool SV, int NW>
-__global__ __launch_bounds__(NW * 64) void k_gemm(GemvArgs A) {
+__global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) void k_gemm(GemvArgs A) {
   extern __shared__ uint32_t lds[];
   constexpr int WPG = QT<BITS>::WPG, HALVES = QT<BITS>::PPW / 4;
   constexpr int GB = SMOE_GM_GB;  // groups per load batch (multiple of 4)
