@@ -166,6 +166,27 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
       return rc;
     if (launched) return SMOE_OK;
   }
+  // the shared expert needs only x: it runs on the layer's side stream from
+  // the work enqueued so far, beside routing and the routed stages, and the
+  // combine waits for it
+  float* ysh = nullptr;
+  if (L.desc.shared_ffn_dim) {
+    float* hsh = (float*)(ws + W.h_shared);
+    ysh = (float*)(ws + W.y_shared);
+    if ((rc = check_hip(hipEventRecord(L.fork, s), "shared-expert fork")) ||
+        (rc = check_hip(hipStreamWaitEvent(L.side, L.fork, 0), "shared-expert fork")))
+      return rc;
+    if ((rc = check_hip(launch_gate_up(L, true, x, xmode, eps, T, T, 1, meta, active, offs,
+                                       pair_token, hsh, L.side, nullptr),
+                        "shared gate/up launch")))
+      return rc;
+    if ((rc = check_hip(launch_down(L, true, hsh, T, T, 1, meta, active, offs, ysh, L.side,
+                                    nullptr),
+                        "shared down launch")))
+      return rc;
+    if ((rc = check_hip(hipEventRecord(L.join, L.side), "shared-expert join")))
+      return rc;
+  }
   if ((rc = check_hip(launch_route(logits, T, E, k, norm, ids, w, uids, uw, 1, meta, active,
                                    offs, pair_token, pair_of, s, cfg),
                       "route launch")))
@@ -177,18 +198,6 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
                    "gate/up launch");
   }
   if (rc) return rc;
-  float* ysh = nullptr;
-  if (L.desc.shared_ffn_dim) {
-    float* hsh = (float*)(ws + W.h_shared);
-    ysh = (float*)(ws + W.y_shared);
-    if ((rc = check_hip(launch_gate_up(L, true, x, xmode, eps, T, T, 1, meta, active, offs,
-                                       pair_token, hsh, s, nullptr),
-                        "shared gate/up launch")))
-      return rc;
-    if ((rc = check_hip(launch_down(L, true, hsh, T, T, 1, meta, active, offs, ysh, s, nullptr),
-                        "shared down launch")))
-      return rc;
-  }
   {
     TracedLaunch t(SMOE_KERNEL_DOWN);
     rc = check_hip(launch_down(L, false, h, T, T * k, max_slots, meta, active, offs, y, s,
@@ -196,6 +205,8 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
                    "down launch");
   }
   if (rc) return rc;
+  if (ysh && (rc = check_hip(hipStreamWaitEvent(s, L.join, 0), "shared-expert join")))
+    return rc;
   return check_hip(
       launch_combine(y, pair_of, w, ysh, cfg.shared_gate, out, T, k, (int)L.desc.d_model,
                      accumulate, s),
@@ -289,8 +300,23 @@ int smoe_load_blobs(const smoe_layer_desc* desc, const void* d_blobs, uint64_t n
   smoe_layer* h = new (std::nothrow) smoe_layer;
   if (!h) return fail(SMOE_E_ARG, "out of host memory");
   h->info = info;
+  if (D.shared_ffn_dim) {
+    hipError_t e = hipStreamCreateWithFlags(&h->info.side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->info.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->info.join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      delete h;
+      return fail(SMOE_E_HIP, "shared-expert stream and events: %s", hipGetErrorString(e));
+    }
+  }
   *out = h;
   return ok();
+}
+
+smoe_layer::~smoe_layer() {
+  if (info.join) (void)hipEventDestroy(info.join);
+  if (info.fork) (void)hipEventDestroy(info.fork);
+  if (info.side) (void)hipStreamDestroy(info.side);
 }
 
 void smoe_free(smoe_layer* layer) { delete layer; }

@@ -59,6 +59,10 @@ struct LayerInfo {
   uint64_t shared_nbytes;
   ExpertPlan plan;
   ExpertPlan shared_plan;  // valid when desc.shared_ffn_dim > 0
+  // shared expert: a stream of the layer's own (default priority) on which
+  // it runs beside routing and the routed stages, and the fork / join events
+  hipStream_t side;
+  hipEvent_t fork, join;
 };
 
 // Input description for the gate/up stage.
@@ -133,4 +137,5 @@ hipError_t launch_quantise(const float* w, int64_t n, int bits, int f16, uint8_t
 // The opaque handle of include/smoe.h: host-side metadata of one layer.
 struct smoe_layer {
   smoe::LayerInfo info;
+  ~smoe_layer();
 };

@@ -159,6 +159,41 @@ def test_repeat_calls_are_bitwise_identical():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("T", [3, 40])
+def test_shared_expert_side_stream_back_to_back(T):
+    """The shared expert runs on the layer's own stream, forked from and
+    joined back into the caller's: several forwards enqueued back to back on
+    one (non-default) stream with one workspace, no synchronisation between
+    them, each equal bit for bit to the same forward run alone."""
+    torch = _torch()
+    import quantised_moe_expert_amd as smoe
+    d, ffn, E, k, sh = 512, 256, 16, 4, 384
+    hl = random_layer(4500 + T, d, ffn, E, 4, "f32", shared_ffn=sh)
+    r = synth.rng(4501 + T)
+    dl = DeviceLayer(hl)
+    xs = [_x(r, T, d, "bf16") for _ in range(4)]
+    lgs = [synth.normal_f32(r, (T, E)) for _ in range(4)]
+    alone = [dl.forward(x, lg, k, True)[0] for x, lg in zip(xs, lgs)]
+    stream = torch.cuda.Stream()
+    nws = smoe.smoe_workspace_bytes(dl.handle, T, k)
+    ws = torch.zeros(nws, dtype=torch.uint8, device="cuda:0")
+    dx = [torch.from_numpy(x).cuda().to(torch.bfloat16) for x in xs]
+    dlg = [torch.from_numpy(lg).cuda() for lg in lgs]
+    outs = [torch.full((T, d), float("nan"), dtype=torch.float32, device="cuda:0")
+            for _ in range(4)]
+    torch.cuda.synchronize()
+    for i in range(4):
+        smoe.smoe_moe_forward(dl.handle, dx[i].data_ptr(), smoe.SMOE_DTYPE_BF16,
+                              dlg[i].data_ptr(), T, k, True, outs[i].data_ptr(), 0, 0,
+                              ws.data_ptr(), nws, stream.cuda_stream)
+    stream.synchronize()
+    for i in range(4):
+        assert np.array_equal(outs[i].cpu().numpy(), alone[i]), i
+    ref, _, _ = O.moe_forward(hl.oracle(), xs[3], lgs[3], k, True)
+    assert rel_l2(alone[3], ref) <= TOL
+    dl.close()
+
+
 def test_single_token_repeated_launches_and_streams():
     # the single-launch kernel's grid barrier must stay consistent across many
     # launches, across layers, and across streams
