@@ -35,10 +35,12 @@
  *  - hip_stream is a hipStream_t (NULL = the legacy default stream). All GPU
  *    work of a call is ordered on it; calls return without synchronising.
  *    A layer with a shared expert runs that expert on a stream of its own
- *    (created by smoe_load_blobs, default priority), forked from hip_stream
- *    at the start of the call and joined back into it before the combine, so
- *    the call's work still completes in hip_stream's order (and is captured
- *    with it into a graph).
+ *    (default priority, created with two events by the layer's first
+ *    forward on the current device, released by smoe_free), forked from
+ *    hip_stream at the start of the call and joined back into it before the
+ *    combine, so the call's work still completes in hip_stream's order (and
+ *    is captured with it into a graph). Capture the first forward of such a
+ *    layer only after one eager forward (stream creation is not capturable).
  *  - Return value: SMOE_OK (0) or a negative SMOE_E_* code. On failure a
  *    message is available from smoe_last_error() (thread-local, valid until
  *    the next call on the same thread). Argument checks happen on the host
@@ -139,11 +141,9 @@ int smoe_expert_layout_of(uint32_t d_model, uint32_t ffn_dim, uint32_t bits,
  *                in the same layout, or NULL when shared_ffn_dim == 0.
  *  shared_nbytes its size (>= its raw size).
  *  out           receives the handle (NULL on failure).
- * No GPU work, no device allocation; with a shared expert it creates one
- * non-blocking stream and two events on the current device (released by
- * smoe_free). Errors: SMOE_E_ARG (bad desc fields or null pointers),
- * SMOE_E_LAYOUT (stride, size or alignment), SMOE_E_UNSUPPORTED (a tensor
- * width this build has no kernel for), SMOE_E_HIP (the stream or events). */
+ * No GPU work, no device allocation. Errors: SMOE_E_ARG (bad desc fields or
+ * null pointers), SMOE_E_LAYOUT (stride, size or alignment), SMOE_E_UNSUPPORTED
+ * (a tensor width this build has no kernel for). */
 int smoe_load_blobs(const smoe_layer_desc* desc, const void* d_blobs, uint64_t nbytes,
                     const void* d_shared_blob, uint64_t shared_nbytes, smoe_layer** out);
 

@@ -140,6 +140,30 @@ int check_hip(hipError_t e, const char* what) {
   return SMOE_OK;
 }
 
+// The shared expert's stream and fork / join events, created on first use
+// (on the current device) so that registering a layer needs no GPU.
+std::mutex g_side_mu;
+
+hipError_t side_stream(const LayerInfo& L) {
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  if (L.side) return hipSuccess;
+  hipStream_t st = nullptr;
+  hipEvent_t f = nullptr, j = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    if (j) (void)hipEventDestroy(j);
+    if (f) (void)hipEventDestroy(f);
+    if (st) (void)hipStreamDestroy(st);
+    return e;
+  }
+  L.fork = f;
+  L.join = j;
+  L.side = st;
+  return hipSuccess;
+}
+
 // One layer: route+group, gate/up+SwiGLU, down, combine (optionally into the
 // residual stream with RMSNorm applied on the way in).
 int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const float* logits,
@@ -173,7 +197,8 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
   if (L.desc.shared_ffn_dim) {
     float* hsh = (float*)(ws + W.h_shared);
     ysh = (float*)(ws + W.y_shared);
-    if ((rc = check_hip(hipEventRecord(L.fork, s), "shared-expert fork")) ||
+    if ((rc = check_hip(side_stream(L), "shared-expert stream and events")) ||
+        (rc = check_hip(hipEventRecord(L.fork, s), "shared-expert fork")) ||
         (rc = check_hip(hipStreamWaitEvent(L.side, L.fork, 0), "shared-expert fork")))
       return rc;
     if ((rc = check_hip(launch_gate_up(L, true, x, xmode, eps, T, T, 1, meta, active, offs,
@@ -300,15 +325,6 @@ int smoe_load_blobs(const smoe_layer_desc* desc, const void* d_blobs, uint64_t n
   smoe_layer* h = new (std::nothrow) smoe_layer;
   if (!h) return fail(SMOE_E_ARG, "out of host memory");
   h->info = info;
-  if (D.shared_ffn_dim) {
-    hipError_t e = hipStreamCreateWithFlags(&h->info.side, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->info.fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->info.join, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      delete h;
-      return fail(SMOE_E_HIP, "shared-expert stream and events: %s", hipGetErrorString(e));
-    }
-  }
   *out = h;
   return ok();
 }

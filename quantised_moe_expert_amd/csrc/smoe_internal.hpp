@@ -61,8 +61,9 @@ struct LayerInfo {
   ExpertPlan shared_plan;  // valid when desc.shared_ffn_dim > 0
   // shared expert: a stream of the layer's own (default priority) on which
   // it runs beside routing and the routed stages, and the fork / join events
-  hipStream_t side;
-  hipEvent_t fork, join;
+  // (created by the layer's first forward that has a shared expert)
+  mutable hipStream_t side;
+  mutable hipEvent_t fork, join;
 };
 
 // Input description for the gate/up stage.
