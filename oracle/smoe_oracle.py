@@ -60,7 +60,7 @@ __all__ = [
     "TensorSpan", "ExpertLayout", "expert_layout",
     "build_expert_blob", "read_expert_tensors",
     "OracleLayer", "route", "softmax64", "silu", "swiglu_expert",
-    "RouteOpts", "route_ex", "sigmoid32",
+    "RouteOpts", "route_ex",
     "moe_forward", "rms_norm", "decode_step",
 ]
 
@@ -170,18 +170,29 @@ def decode_codes(codes: np.ndarray, scale: float, bits: int) -> np.ndarray:
 
 
 def dequantise(packed: np.ndarray, scales: np.ndarray, rows: int, cols: int,
-               bits: int, group: int = GROUP_SIZE) -> np.ndarray:
+               bits: int, group: int = GROUP_SIZE,
+               out: Optional[np.ndarray] = None) -> np.ndarray:
     """Dense float64 [rows, cols] weight. Flat element i (row-major) uses
     scale[i // group]; groups run over the flattened tensor and may straddle
-    rows when cols is not a multiple of the group."""
+    rows when cols is not a multiple of the group. `out` (optional, float64,
+    rows * cols elements) receives the result."""
     n = int(rows) * int(cols)
-    codes = unpack_codes(packed, n, bits).astype(np.float64)
+    codes = unpack_codes(packed, n, bits)
     s = np.asarray(scales).reshape(-1).astype(np.float64)
-    if s.size < scale_count(n, group):
+    ng = scale_count(n, group)
+    if s.size < ng:
         raise ValueError("too few scales")
-    m = level_midpoint(bits)
-    idx = np.arange(n) // group
-    return ((codes - m) / m * s[idx]).reshape(int(rows), int(cols))
+    w = np.empty(n, np.float64) if out is None else out.reshape(-1)
+    if w.size != n or w.dtype != np.float64:
+        raise ValueError("out must hold rows * cols float64 values")
+    # the level (c - m)/m of every code from the table of all 2^bits levels
+    # (the same float64 values), times the scale of its group
+    np.take(level_table(bits), codes, out=w)
+    if n % group == 0:
+        w.reshape(ng, group)[...] *= s[:ng, None]
+    else:
+        w *= s[np.arange(n) // group]
+    return w.reshape(int(rows), int(cols))
 
 
 # --------------------------------------------------------------------------
@@ -316,18 +327,21 @@ def build_expert_blob(layout: ExpertLayout,
     return blob
 
 
-def read_expert_tensors(blob: np.ndarray, layout: ExpertLayout
+def read_expert_tensors(blob: np.ndarray, layout: ExpertLayout,
+                        out: Optional[Dict[str, np.ndarray]] = None
                         ) -> Dict[str, np.ndarray]:
-    """Dense float64 gate, up, down weights of one expert blob."""
+    """Dense float64 gate, up, down weights of one expert blob (into the
+    arrays of `out` when given, one per tensor name)."""
     b = np.asarray(blob, dtype=np.uint8).reshape(-1)
     st = _SCALE_DTYPES[layout.scale_dtype]
-    out = {}
+    res = {}
     for name, span in layout.spans().items():
         codes = b[span.codes_offset: span.codes_offset + span.codes_bytes]
         scales = b[span.scales_offset: span.scales_offset + span.scales_bytes
                    ].copy().view(st)
-        out[name] = dequantise(codes, scales, span.rows, span.cols, layout.bits)
-    return out
+        res[name] = dequantise(codes, scales, span.rows, span.cols, layout.bits,
+                               out=None if out is None else out[name])
+    return res
 
 
 # --------------------------------------------------------------------------
@@ -392,13 +406,6 @@ class RouteOpts:
                 and self.mask is None and self.shared_gate is None)
 
 
-def sigmoid32(l32: np.ndarray) -> np.ndarray:
-    """sigmoid in float32 arithmetic: 1 / (1 + exp(-x))."""
-    l32 = np.asarray(l32, dtype=np.float32)
-    with np.errstate(over="ignore"):
-        return (np.float32(1.0) / (np.float32(1.0) + np.exp(-l32))).astype(np.float32)
-
-
 def route_ex(logits_row: np.ndarray, top_k: int, norm_topk_prob: bool,
              opts: "RouteOpts") -> Tuple[List[int], np.ndarray]:
     """Top-k routing with the variants of RouteOpts, in the order the format
@@ -408,10 +415,10 @@ def route_ex(logits_row: np.ndarray, top_k: int, norm_topk_prob: bool,
     factor.
 
     Without a bias the selection compares the fp32 logits (the scores are
-    monotone in them); with a bias it compares fp32 score + bias, the score
-    computed in fp32 (1/(1+exp(-x)), or exp(x - max)/sum over the routable
-    experts), which is the precision the kernels decide in. Weights are fp64
-    except the fp32 scores that selection used."""
+    monotone in them, and the logits are exact); with a bias it compares the
+    float64 sum score + bias, the score being the float64 softmax or sigmoid
+    of the fp32 logits and the bias its fp32 value taken exactly. Weights are
+    float64."""
     l32 = np.asarray(logits_row, dtype=np.float32).reshape(-1)
     E = l32.size
     mask = np.ones(E, dtype=bool) if opts.mask is None else opts.mask.reshape(-1)
@@ -420,24 +427,17 @@ def route_ex(logits_row: np.ndarray, top_k: int, norm_topk_prob: bool,
     routable = [e for e in range(E) if mask[e]]
     if not (1 <= top_k <= min(MAX_TOP_K, len(routable))):
         raise ValueError(f"top_k must be in [1, min(16, routable experts)], got {top_k}")
-    if opts.expert_bias is None:
-        keyv = [float(v) for v in l32]
-    else:
-        if opts.sigmoid:
-            sc32 = sigmoid32(l32)
-        else:
-            lr = l32[mask]
-            ex = np.exp((l32 - np.max(lr)).astype(np.float32)).astype(np.float32)
-            den = np.float32(np.sum(ex[mask], dtype=np.float32))
-            sc32 = (ex / den).astype(np.float32)
-        b32 = opts.expert_bias.reshape(-1).astype(np.float32)
-        keyv = [float(np.float32(sc32[e] + b32[e])) for e in range(E)]
-    ids = sorted(routable, key=lambda e: (-keyv[e], e))[:top_k]
     if opts.sigmoid:
         p = 1.0 / (1.0 + np.exp(-l32.astype(np.float64)))
     else:
         p = np.zeros(E, dtype=np.float64)
         p[mask] = softmax64(l32[mask])
+    if opts.expert_bias is None:
+        keyv = [float(v) for v in l32]
+    else:
+        b64 = opts.expert_bias.reshape(-1).astype(np.float64)
+        keyv = [float(p[e] + b64[e]) for e in range(E)]
+    ids = sorted(routable, key=lambda e: (-keyv[e], e))[:top_k]
     w = np.array([p[e] for e in ids], dtype=np.float64)
     if norm_topk_prob:
         w = w / np.sum(w)
@@ -493,6 +493,14 @@ class OracleLayer:
                 b = self.blobs[e * self.stride: e * self.stride + self.layout.raw_size]
             self._cache[e] = read_expert_tensors(b, self.layout)
         return self._cache[e]
+
+    def expert_weights_into(self, e: int, out: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+        """As expert_weights, into caller-owned float64 arrays (not cached)."""
+        if self.expert_blobs is not None and e in self.expert_blobs:
+            b = self.expert_blobs[e]
+        else:
+            b = self.blobs[e * self.stride: e * self.stride + self.layout.raw_size]
+        return read_expert_tensors(b, self.layout, out=out)
 
     def shared_weights(self) -> Optional[Dict[str, np.ndarray]]:
         if self.shared_layout is None:

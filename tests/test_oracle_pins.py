@@ -202,6 +202,57 @@ def test_mse_grid_matches_brute_force(bits):
         assert i == bi and s == bs
 
 
+def test_f16_candidate_roundings_worked_by_hand(golden):
+    # the fixture's fp16 values are derived by hand from the fp16 format
+    # (11-bit significand, subnormal step 2^-24, ties to even)
+    for row in golden("f16_scale_candidates.txt"):
+        absmax, i, prod, want = float(row[0]), int(row[1]), float(row[2]), float(row[3])
+        assert O.candidate_fractions()[i] * absmax == prod
+        assert float(np.float16(prod)) == want
+
+
+def test_f16_scale_is_the_rounded_candidate():
+    # "SMOE Quantisation", L2-MSE Scale Optimiser, with fp16 storage: a group
+    # lying on the level grid of the fp16 value of its absmax candidate (and
+    # whose absmax element is 1 + 2^-11 or 1 + 3 * 2^-11, halfway between two
+    # fp16 values) is stored with the tie-to-even fp16 scale: 1.0 and
+    # 1 + 2^-9, not the fp32 values of the candidates
+    r = np.random.default_rng(9)
+    for absmax, want in ((1.00048828125, 1.0), (1.00146484375, 1.001953125)):
+        for bits in (2, 4):
+            lv = O.level_table(bits)
+            # codes below the top level, so no element but the first reaches
+            # the scale; the first is the absmax, just off the grid
+            codes = r.integers(1, (1 << bits) - 1, 64)
+            w = lv[codes] * want
+            w[0] = absmax
+            s16, c16, i16 = O.mse_grid_scale(w, bits, "f16")
+            assert i16 == 63 and s16 == want
+            s32, _, i32 = O.mse_grid_scale(w, bits, "f32")
+            assert s32 != want
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_mse_grid_f16_matches_brute_force(bits):
+    # exhaustive search over (candidate, code) pairs with every candidate
+    # stored as fp16 (the rounding pinned by the fixture above)
+    lv = O.level_table(bits)
+    r = np.random.default_rng(23)
+    for _ in range(25):
+        w = r.standard_normal(64) * 0.02
+        w[r.integers(0, 64)] *= 10
+        a = float(np.max(np.abs(w)))
+        best = None
+        for i, f in enumerate(O.candidate_fractions()):
+            sc = float(np.float16(f * a))
+            err = np.min((w[:, None] - lv[None, :] * sc) ** 2, axis=1).sum()
+            if best is None or err < best[0] - 1e-18:
+                best = (err, i, sc)
+        s, codes, i = O.mse_grid_scale(w, bits, "f16")
+        assert i == best[1] and s == best[2]
+        assert abs(_mse_with_table(w, s, codes, bits) - best[0]) <= 1e-15 * max(1.0, best[0])
+
+
 def test_outlier_group_picks_smaller_scale():
     # "SMOE Quantisation", L2-MSE Scale Optimiser: one loud outlier among
     # near-zero weights pulls the scale below absmax
@@ -462,6 +513,47 @@ def test_rms_norm_closed_forms():
     ratio = np.sqrt(ms + 1e-6) / np.sqrt(ms + 1e-6 / 1e6)
     assert np.allclose(O.rms_norm(h * 1e3), O.rms_norm(h) * ratio, rtol=1e-12)
     assert not np.allclose(O.rms_norm(h * 1e3), O.rms_norm(h), rtol=1e-9)
+
+
+def test_decode_step_norm_placement_closed_form():
+    # ".smoe Binary Format", Arch Block (rms eps 1e-6): each layer adds
+    # MoE(rms_norm(h)) to h. One expert with every code 12 (level 4.5 / 7.5 =
+    # 0.6) and every scale 2^-7, on a constant h = a: rms_norm(h) is the
+    # constant nu = a / sqrt(a^2 + eps), gate = up = 0.6 * 2^-7 * d * nu on
+    # every row, and the down output is 0.6 * 2^-7 * ffn * silu(g) * g on
+    # every element. Dropping the norm, applying it after the layer, or
+    # taking eps outside the root gives a different value.
+    d, ffn, L, s = 64, 64, 0.6, 2.0 ** -7
+    lay = O.expert_layout(d, ffn, 4, "f32")
+    blob = np.zeros(lay.padded_size, np.uint8)
+    for span in lay.spans().values():
+        blob[span.codes_offset: span.codes_offset + span.codes_bytes] = 0xCC  # codes 12, 12
+        blob[span.scales_offset: span.scales_offset + span.scales_bytes] = \
+            np.full(span.n_scales, s, np.float32).view(np.uint8)
+    layer = O.OracleLayer(d, ffn, 1, 4, blob)
+    lg = [np.zeros((1, 1), np.float32)] * 2
+
+    def silu(v):
+        return v / (1.0 + math.exp(-v))
+
+    for a in (0.5, 1e-3):
+        x = np.full((1, d), a)
+        h = O.decode_step([layer, layer], x, lg, 1, True)
+        want = a
+        for _ in range(2):
+            nu = want / math.sqrt(want * want + 1e-6)
+            g = L * s * d * nu
+            want = want + L * s * ffn * silu(g) * g
+        assert np.allclose(h, want, rtol=1e-13, atol=0)
+        # the same layer without the norm, or with eps outside the root
+        g_raw = L * s * d * a
+        assert abs((a + L * s * ffn * silu(g_raw) * g_raw) - h[0, 0]) > 1e-9
+        nu_bad = a / (math.sqrt(a * a) + 1e-6)
+        g_bad = L * s * d * nu_bad
+        one_bad = a + L * s * ffn * silu(g_bad) * g_bad
+        nu1 = a / math.sqrt(a * a + 1e-6)
+        one = a + L * s * ffn * silu(L * s * d * nu1) * (L * s * d * nu1)
+        assert abs(one_bad - one) > 1e-12 or a == 0.5
 
 
 def test_decode_step_zero_layers_keep_residual_and_chain():

@@ -120,3 +120,32 @@ def test_shared_gate_weights_the_shared_expert():
     S = 2.0 * (plain - zero_gate)
     assert np.allclose(ln3_gate, plain - S / 4.0, rtol=1e-6, atol=1e-9)
     assert np.max(np.abs(S)) > 0.0
+
+
+def test_biased_selection_is_decided_in_float64():
+    # 2.2 MoE: the bias is added to the score for the selection. Two equal
+    # logits but for 2^-20: softmax scores 1/2 -+ tanh(2^-21) (closed form),
+    # and a bias on expert 0 of 2^-21 - 2^-30 (exact in fp32). The exact keys
+    # differ by 2^-30 - (tanh(2^-21) - 2^-21), i.e. expert 1 is ahead by
+    # about 2^-30; an fp32 sum would round both keys to 1/2 + 2^-22 and the
+    # tie would go to expert 0.
+    d = 2.0 ** -20
+    lg = np.array([0.0, d], dtype=np.float32)
+    assert float(lg[1]) == d
+    bias = np.array([2.0 ** -21 - 2.0 ** -30, 0.0], dtype=np.float32)
+    assert float(bias[0]) == 2.0 ** -21 - 2.0 ** -30
+    p0, p1 = 0.5 - math.tanh(d / 2) / 2, 0.5 + math.tanh(d / 2) / 2
+    assert (p0 + float(bias[0])) < p1                      # exact order: 1 first
+    assert np.float32(np.float32(p0) + bias[0]) == np.float32(p1)  # fp32 ties
+    ids, w = O.route_ex(lg, 1, False, O.RouteOpts(expert_bias=bias))
+    assert ids == [1]
+    assert abs(w[0] - p1) < 1e-15
+    ids, _ = O.route_ex(lg, 2, False, O.RouteOpts(expert_bias=bias))
+    assert ids == [1, 0]
+    # the same with sigmoid scoring: sigmoid(0) = 1/2, sigmoid(2^-20) =
+    # 1/2 + tanh(2^-21)/2 in closed form
+    s1 = 0.5 + math.tanh(d / 2) / 2
+    b2 = np.array([2.0 ** -22 - 2.0 ** -31, 0.0], dtype=np.float32)
+    assert (0.5 + float(b2[0])) < s1
+    ids, w = O.route_ex(lg, 1, False, O.RouteOpts(sigmoid=True, expert_bias=b2))
+    assert ids == [1] and abs(w[0] - s1) < 1e-15
