@@ -5,7 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "smoe_gemv.hpp"
+#include "smoe_device.hpp"
 #include "smoe_gemv_args.hpp"
 #include "smoe_internal.hpp"
 
@@ -107,6 +107,20 @@ __device__ __forceinline__ float rt_wave_sum(float v) {
   return rt_lane63(v);
 }
 
+// Float64 sum / max over the wave. The butterfly adds in a different order
+// on each lane, so the sum is lane 0's, broadcast: every lane divides by the
+// same value.
+__device__ __forceinline__ double rt_wave_sum64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return __shfl(v, 0, 64);
+}
+__device__ __forceinline__ double rt_wave_max64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
 // Top-k of one token per wave, over as many workgroups as tokens need:
 // EPL = logits per lane (E <= 64 * EPL).
 constexpr int TOPK_THREADS = 256;
@@ -156,21 +170,73 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(RouteArgs A) {
 #pragma unroll
       for (int i = 0; i < EPL; ++i) sc[i] = sc[i] / se;
     }
-    // selection keys (see rt_key; 0 = not routable): the logit, or with a
-    // bias the fp32 score + bias
+    float wsum = 0.f;
+    float wj[SMOE_MAX_TOP_K];
+    int idj[SMOE_MAX_TOP_K];
+    if (A.cfg.bias) {
+      // with a bias: k rounds over the float64 key score + bias (the score
+      // the float64 softmax over the routable logits, or the sigmoid; the
+      // fp32 logits and bias taken exactly); the largest key wins, equal
+      // keys go to the lowest id (ballots over the slots in id order)
+      double kb[EPL];
+      bool taken[EPL];
+      if (!A.cfg.sigmoid) {
+        double se = 0.0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          kb[i] = ok[i] ? exp((double)lv[i] - (double)mx) : 0.0;
+          se += kb[i];
+        }
+        se = rt_wave_sum64(se);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) kb[i] = kb[i] / se;
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) kb[i] = 1.0 / (1.0 + exp(-(double)lv[i]));
+      }
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        kb[i] += (double)A.cfg.bias[min(e, A.E - 1)];
+        taken[i] = !ok[i];
+      }
+#pragma unroll
+      for (int j = 0; j < SMOE_MAX_TOP_K; ++j) {
+        if (j < A.k) {
+          double m = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < EPL; ++i)
+            if (!taken[i]) m = fmax(m, kb[i]);
+          m = rt_wave_max64(m);
+          int id = -1;
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            const uint64_t b = __ballot(!taken[i] && kb[i] == m);
+            if (id < 0 && b) id = 64 * i + (int)__builtin_ctzll(b);
+          }
+          float p = 0.f;
+#pragma unroll
+          for (int i = 0; i < EPL; ++i)
+            if (lane + 64 * i == id) {
+              taken[i] = true;
+              p = sc[i];
+            }
+          p = rt_lane_value(p, id & 63);
+          wj[j] = p;
+          idj[j] = id;
+          wsum += p;
+        }
+      }
+    } else {
+    // selection keys (see rt_key; 0 = not routable): the logit
     uint64_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      const float b = A.cfg.bias ? A.cfg.bias[min(e, A.E - 1)] : 0.f;
-      const float kv = A.cfg.bias ? sc[i] + b : lv[i];
-      key[i] = ok[i] ? rt_key(kv, e) : 0;
+      key[i] = ok[i] ? rt_key(lv[i], e) : 0;
     }
     // k rounds: the largest remaining key over the wave wins, its owner
     // drops it and broadcasts the winner's score
-    float wsum = 0.f;
-    float wj[SMOE_MAX_TOP_K];
-    int idj[SMOE_MAX_TOP_K];
 #pragma unroll
     for (int j = 0; j < SMOE_MAX_TOP_K; ++j) {
       if (j < A.k) {
@@ -191,6 +257,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(RouteArgs A) {
         idj[j] = id;
         wsum += p;
       }
+    }
     }
     // lane j < k writes selection j
 #pragma unroll
@@ -387,14 +454,6 @@ hipError_t launch_combine(const float* y, const int* pair_of, const float* w,
 // -------------------------------------------------------------- dispatch --
 
 
-static bool v_supported(int v) {
-#define SMOE_V_CASE(n) \
-  if (v == n) return true;
-  SMOE_V_LIST(SMOE_V_CASE)
-#undef SMOE_V_CASE
-  return false;
-}
-
 bool plan_matrix(int rows, int cols, int bits, uint64_t codes_off, uint64_t scales_off,
                  MatPlan* out) {
   if (cols % 64 || rows <= 0) return false;
@@ -402,52 +461,12 @@ bool plan_matrix(int rows, int cols, int bits, uint64_t codes_off, uint64_t scal
   int lg = 0;
   while (lg < 6 && (W % (2 << lg)) == 0) ++lg;
   const int v = W >> lg;
-  if (!v_supported(v)) return false;
   *out = MatPlan{codes_off, scales_off, rows, cols, W, v, lg};
   return true;
 }
 
 static MatArgs mat_args(const MatPlan& m) {
   return MatArgs{m.codes_off, m.scales_off, m.rows, m.cols, m.words_per_row, m.lpr_log2};
-}
-
-template <int BITS, typename ST>
-static hipError_t gate_up_dispatch(int v, int in, dim3 grid, unsigned lds, hipStream_t s,
-                                   const GemvArgs& A) {
-#define SMOE_GU_CASE(n) \
-  if (v == n) return launch_gu<BITS, ST, n>(A, in, grid, lds, s);
-  SMOE_V_LIST(SMOE_GU_CASE)
-#undef SMOE_GU_CASE
-  return hipErrorInvalidValue;
-}
-
-template <int BITS, typename ST>
-static hipError_t down_dispatch(int v, dim3 grid, unsigned lds, hipStream_t s, const GemvArgs& A) {
-#define SMOE_DN_CASE(n) \
-  if (v == n) return launch_dn<BITS, ST, n>(A, grid, lds, s);
-  SMOE_V_LIST(SMOE_DN_CASE)
-#undef SMOE_DN_CASE
-  return hipErrorInvalidValue;
-}
-
-// Launch shape of a grouped stage over `slots` expert slots: rows per wave
-// (whole row groups, up to 8, fewer when that leaves under ~2048 workgroups)
-// and tokens staged per chunk (as many as fit in 48 KB of LDS, at most 8).
-static void grouped_shape(const MatPlan& m, bool split, int slots, GemvArgs& A, dim3& grid,
-                          unsigned& lds) {
-  const int RPW = 64 >> m.lpr_log2, LPR = 1 << m.lpr_log2;
-  const int groups = (m.rows + RPW - 1) / RPW;
-  int gpw = (int)((int64_t)groups * slots / (GV_WAVES * 2048));
-  gpw = gpw < 1 ? 1 : (gpw > 8 ? 8 : gpw);
-  A.rows_per_wave = gpw * RPW;
-  const int rpb = A.rows_per_wave * GV_WAVES;
-  grid = dim3((m.rows + rpb - 1) / rpb, slots);
-  const int nk = m.v / 4 + m.v % 4;
-  const int per_token = (m.cols / 2 * (split ? 2 : 1) + nk * LPR + 1 + GV_WAVES * 2) * 4;
-  int tc = 49152 / per_token;
-  tc = tc < 1 ? 1 : (tc > 8 ? 8 : tc);
-  A.tc = tc;
-  lds = (unsigned)gv_lds_layout(m.cols, LPR, nk, tc, split).total * 4;
 }
 
 // Launch shape of a matrix-core stage: 16-row tiles, one per wave, or one
@@ -460,22 +479,16 @@ static void grouped_shape(const MatPlan& m, bool split, int slots, GemvArgs& A, 
 // rows) the workgroup has eight waves and up to 160 KB, one per CU, so the
 // weights are read fewer times. The k-split partial-sum region (last in the
 // layout) is allocated only when used. False when not even one token fits.
-#ifndef SMOE_GM_TPW_MAX
-#define SMOE_GM_TPW_MAX 4
-#endif
-#ifndef SMOE_GM_TC_MIN
-#define SMOE_GM_TC_MIN 8
-#endif
+constexpr int GM_TPW_MAX = 4;  // 16-row tiles per wave, at most
+constexpr int GM_TC_MIN = 8;   // tokens per chunk, at least
 // (512 measured best against 256, 384, 1024 and 3000 on the 8- and 32-token
 // layers: fewer, longer workgroups while two rounds still fill the GPU)
-#ifndef SMOE_GM_MIN_WG
-#define SMOE_GM_MIN_WG 512
-#endif
+constexpr int GM_MIN_WG = 512;
 static bool gm_shape(const MatPlan& m, bool split, int pairs, int slots, GemvArgs& A, dim3& grid,
                      unsigned& lds, int& nw) {
   const int tiles = (m.rows + 15) / 16;
   const int mean = (pairs + slots - 1) / slots;
-  const int want = 2 * mean < SMOE_GM_TC_MIN ? SMOE_GM_TC_MIN : (2 * mean > 16 ? 16 : 2 * mean);
+  const int want = 2 * mean < GM_TC_MIN ? GM_TC_MIN : (2 * mean > 16 ? 16 : 2 * mean);
   auto bytes = [&](int t, int w, int k) {
     const GmLds L = gm_lds_layout(m.cols, t, split, w);
     return (k > 1 ? L.total : L.part) * 4;
@@ -485,12 +498,12 @@ static bool gm_shape(const MatPlan& m, bool split, int pairs, int slots, GemvArg
   const int ks = nw == 4 && (int64_t)(tiles + nw - 1) / nw * slots < 1024 ? nw : 1;
   A.ksplit = ks;
   const int tpb = nw / ks;
-  // tiles per wave: more while the grid keeps over SMOE_GM_MIN_WG
+  // tiles per wave: more while the grid keeps over GM_MIN_WG
   // workgroups, so that each staging of the tokens serves more rows
   int tpw = 1;
   if (ks == 1)
-    while (tpw < SMOE_GM_TPW_MAX &&
-           (int64_t)((tiles + tpb * 2 * tpw - 1) / (tpb * 2 * tpw)) * slots >= SMOE_GM_MIN_WG)
+    while (tpw < GM_TPW_MAX &&
+           (int64_t)((tiles + tpb * 2 * tpw - 1) / (tpb * 2 * tpw)) * slots >= GM_MIN_WG)
       tpw *= 2;
   A.tiles_per_wave = tpw;
   grid = dim3((tiles + tpb * tpw - 1) / (tpb * tpw), slots);
@@ -503,6 +516,11 @@ static bool gm_shape(const MatPlan& m, bool split, int pairs, int slots, GemvArg
   return true;
 }
 
+bool batch_fits(const MatPlan& m, bool split) {
+  // one token staged by a four-wave workgroup, k-split partial sums included
+  return (int64_t)gm_lds_layout(m.cols, 1, split, 4).total * 4 <= 65536;
+}
+
 template <typename ST>
 static hipError_t gm_dispatch(int bits, const GemvArgs& A, bool gate_up, int in, int nw,
                               dim3 grid, unsigned lds, hipStream_t s) {
@@ -512,12 +530,10 @@ static hipError_t gm_dispatch(int bits, const GemvArgs& A, bool gate_up, int in,
 
 // Slots averaging this many routed pairs or more take the K-sliced stage
 // (64 tokens per weight read) instead of 16-token chunks.
-#ifndef SMOE_GMK_MIN_MEAN
-#define SMOE_GMK_MIN_MEAN 24
-#endif
+constexpr int GMK_MIN_MEAN = 24;
 
 bool gmk_wanted(int pairs, int slots) {
-  return slots > 0 && pairs / slots >= SMOE_GMK_MIN_MEAN;
+  return slots > 0 && pairs / slots >= GMK_MIN_MEAN;
 }
 
 static uint64_t al256(uint64_t v) { return (v + 255) / 256 * 256; }
@@ -674,15 +690,8 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
     return L.desc.scale_dtype == SMOE_SCALE_F32
                ? gm_dispatch<float>(L.desc.bits, A, true, in, nw, grid, lds, stream)
                : gm_dispatch<_Float16>(L.desc.bits, A, true, in, nw, grid, lds, stream);
-  grouped_shape(P.gate, in == GV_F32_SPLIT, shared ? 1 : max_slots, A, grid, lds);
-  const int v = P.gate.v;
-  if (L.desc.bits == 4)
-    return L.desc.scale_dtype == SMOE_SCALE_F32
-               ? gate_up_dispatch<4, float>(v, in, grid, lds, stream, A)
-               : gate_up_dispatch<4, _Float16>(v, in, grid, lds, stream, A);
-  return L.desc.scale_dtype == SMOE_SCALE_F32
-             ? gate_up_dispatch<2, float>(v, in, grid, lds, stream, A)
-             : gate_up_dispatch<2, _Float16>(v, in, grid, lds, stream, A);
+  // unreachable for a registered layer (batch_fits is checked at load)
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int pairs,
@@ -713,14 +722,8 @@ hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, i
     return L.desc.scale_dtype == SMOE_SCALE_F32
                ? gm_dispatch<float>(L.desc.bits, A, false, GV_F32, nw, grid, lds, stream)
                : gm_dispatch<_Float16>(L.desc.bits, A, false, GV_F32, nw, grid, lds, stream);
-  grouped_shape(P.down, false, shared ? 1 : max_slots, A, grid, lds);
-  const int v = P.down.v;
-  if (L.desc.bits == 4)
-    return L.desc.scale_dtype == SMOE_SCALE_F32
-               ? down_dispatch<4, float>(v, grid, lds, stream, A)
-               : down_dispatch<4, _Float16>(v, grid, lds, stream, A);
-  return L.desc.scale_dtype == SMOE_SCALE_F32 ? down_dispatch<2, float>(v, grid, lds, stream, A)
-                                              : down_dispatch<2, _Float16>(v, grid, lds, stream, A);
+  // unreachable for a registered layer (batch_fits is checked at load)
+  return hipErrorInvalidValue;
 }
 
 }  // namespace smoe

@@ -15,8 +15,8 @@ TOL = 1e-3
 
 def _torch():
     import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
+    # a GPU test fails where no device is visible (it must not pass by skipping)
+    assert torch.cuda.is_available(), "no GPU visible to torch"
     return torch
 
 
@@ -104,3 +104,31 @@ def test_forward_ex_matches_oracle_with_shared_gate(kind, T):
     o = out.cpu().numpy()
     assert np.all(np.isfinite(o))
     assert rel_l2(o, ref) <= TOL
+
+
+@pytest.mark.parametrize("sigmoid", [False, True])
+def test_biased_near_tie_decided_in_float64(sigmoid):
+    # the near-tie pinned for the oracle (CPU, closed form): two logits 2^-20
+    # apart and a bias on expert 0 just short of the score gap. Float64
+    # score + bias puts expert 1 first; an fp32 sum would tie and pick
+    # expert 0.
+    torch = _torch()
+    import quantised_moe_expert_amd as smoe
+    E = 2
+    lg = np.array([[0.0, 2.0 ** -20]], np.float32)
+    bias = np.zeros(E, np.float32)
+    bias[0] = (2.0 ** -22 - 2.0 ** -31) if sigmoid else (2.0 ** -21 - 2.0 ** -30)
+    ro = O.RouteOpts(sigmoid=sigmoid, expert_bias=bias)
+    for k in (1, 2):
+        want, wt = O.route_ex(lg[0], k, False, ro)
+        assert want == [1, 0][:k]
+        d_lg = torch.from_numpy(lg).cuda()
+        d_bias = torch.from_numpy(bias).cuda()
+        opts = smoe.make_route_opts(sigmoid=sigmoid, d_expert_bias=d_bias.data_ptr())
+        ids = torch.full((1, k), -1, dtype=torch.int32, device="cuda")
+        w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+        smoe.smoe_route_ex(d_lg.data_ptr(), 1, E, k, False, opts, ids.data_ptr(), w.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert ids.cpu().numpy()[0].tolist() == want
+        assert np.allclose(w.cpu().numpy()[0], wt, rtol=1e-5, atol=1e-7)
