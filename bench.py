@@ -92,7 +92,8 @@ def main():
     def make_bank(E, ffn, layout, stride_):
         """E experts at `stride_`: uniform code bytes, lognormal fp32 scales,
         zero padding; offsets from the library's layout query."""
-        bank = torch.randint(0, 256, (E, stride_), dtype=torch.uint8, device=dev, generator=gen)
+        bank = smoe.aligned_buffer(E * stride_, device=dev).view(E, stride_)
+        bank.random_(0, 256, generator=gen)
         for t in (layout.gate, layout.up, layout.down):
             sc = bank[:, t.scales_offset: t.scales_offset + t.scales_bytes].view(torch.float32)
             sc.copy_(torch.empty(sc.shape, device=dev).log_normal_(
@@ -183,7 +184,7 @@ def main():
     # per-launch timing of the two expert kernels: HIP events recorded by the
     # library immediately around the launch, on the launch's stream, one pair
     # per forward, in a pass of its own after the timed loop
-    single = T == 1 and not W.shared_ffn_dim and os.environ.get("SMOE_FORCE_MULTI_KERNEL") != "1"
+    single = T == 1 and not W.shared_ffn_dim
     x_bytes = T * W.d_model * (2 if W.x_dtype == "bf16" else 4)
     gu_raw = sum(t.codes_bytes + t.scales_bytes for t in (lay.gate, lay.up))
     dn_raw = lay.down.codes_bytes + lay.down.scales_bytes
@@ -445,7 +446,7 @@ def bench_offload(args):
     stride, raw, E, k = lay.padded_size, lay.raw_size, W.num_experts, W.top_k
     gen = torch.Generator(device=dev)
     gen.manual_seed(args.seed)
-    host = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
+    host = smoe.aligned_buffer(E * stride, pin_memory=True).view(E, stride)
     for e in range(E):  # uniform code bytes, lognormal fp32 scales, zero padding
         b = torch.randint(0, 256, (stride,), dtype=torch.uint8, device=dev, generator=gen)
         for t in (lay.gate, lay.up, lay.down):
@@ -455,7 +456,7 @@ def bench_offload(args):
         b[raw:] = 0
         host[e].copy_(b)
     torch.cuda.synchronize()
-    cache = torch.empty(max(slots, 1) * stride, dtype=torch.uint8, device=dev)
+    cache = smoe.aligned_buffer(max(slots, 1) * stride, device=dev)
     table = torch.zeros(E, dtype=torch.int64, device=dev)
     desc = smoe.make_desc(W.d_model, W.ffn_dim, E, W.bits, stride, smoe.SMOE_SCALE_F32)
     off = smoe.smoe_offload_create(desc, host.data_ptr(), host.numel(), 0, 0,
@@ -535,7 +536,7 @@ def bench_offload(args):
 
 KERNEL_SOURCES = {
     "gate_up": ("smoe_decode.hpp", "smoe_decode_args.hpp", "smoe_device.hpp"),
-    "gate_up_grouped": ("smoe_gemm.hpp", "smoe_gemv.hpp", "smoe_gemv_args.hpp", "smoe_device.hpp"),
+    "gate_up_grouped": ("smoe_gemm.hpp", "smoe_gemv_args.hpp", "smoe_device.hpp"),
 }
 
 

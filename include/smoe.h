@@ -84,7 +84,10 @@ extern "C" {
 #define SMOE_MAX_TOP_K 16        /* routing width cap                         */
 #define SMOE_MAX_EXPERTS 512     /* routed experts per layer                  */
 #define SMOE_MAX_TOKENS 4096     /* tokens per smoe_moe_forward call          */
-#define SMOE_BANK_ALIGN 256      /* required alignment of blob base pointers  */
+/* Required alignment of the expert bank and shared-blob base pointers: the
+ * 16 KB page boundary every .smoe blob starts on (".smoe Binary Format",
+ * Immutable Encoding; "Model Agnosticism", Dynamic Buffer Allocation). */
+#define SMOE_BANK_ALIGN 16384
 
 /* Description of one MoE layer's expert bank. */
 typedef struct smoe_layer_desc {
@@ -138,12 +141,16 @@ int smoe_expert_layout_of(uint32_t d_model, uint32_t ffn_dim, uint32_t bits,
  *                SMOE_BANK_ALIGN-aligned. Borrowed until smoe_free.
  *  nbytes        size of the bank; must be >= (E-1)*blob_stride + raw_size.
  *  d_shared_blob device pointer to one blob of shape (d_model, shared_ffn_dim)
- *                in the same layout, or NULL when shared_ffn_dim == 0.
+ *                in the same layout, SMOE_BANK_ALIGN-aligned, or NULL when
+ *                shared_ffn_dim == 0.
  *  shared_nbytes its size (>= its raw size).
  *  out           receives the handle (NULL on failure).
  * No GPU work, no device allocation. Errors: SMOE_E_ARG (bad desc fields or
  * null pointers), SMOE_E_LAYOUT (stride, size or alignment), SMOE_E_UNSUPPORTED
- * (a tensor width this build has no kernel for). */
+ * (a tensor width this build has no kernel for, or an activation vector too
+ * long for the batched stages' 64 KB LDS staging: d_model above 11392 with
+ * fp32 hi/lo staging, or ffn_dim above 19072 for any shared or routed
+ * expert). */
 int smoe_load_blobs(const smoe_layer_desc* desc, const void* d_blobs, uint64_t nbytes,
                     const void* d_shared_blob, uint64_t shared_nbytes, smoe_layer** out);
 
@@ -179,7 +186,9 @@ int smoe_route(const float* d_logits, int n_tokens, int n_experts, int top_k,
  *  d_expert_bias     device [num_experts] fp32, nullable: added to the
  *                    scores for the top-k selection only (the weights stay
  *                    the unbiased scores). With a bias the selection
- *                    compares fp32 score + bias; without one it compares
+ *                    compares float64 score + bias (the score recomputed in
+ *                    float64 from the fp32 logits, the bias taken exactly),
+ *                    equal keys to the lower id; without one it compares
  *                    the logits (the same order).
  *  d_shared_gate     device [n_tokens] fp32, nullable: per-token logits of
  *                    the shared-expert gate; the shared expert's output is

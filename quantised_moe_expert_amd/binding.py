@@ -34,6 +34,8 @@ SMOE_MAX_TOP_K = 16
 SMOE_MAX_EXPERTS = 512
 SMOE_MAX_TOKENS = 4096
 SMOE_MAX_QUANT_ELEMENTS = 1 << 31
+SMOE_BLOB_ALIGN = 16384
+SMOE_BANK_ALIGN = 16384
 
 SMOE_KERNEL_NONE = 0
 SMOE_KERNEL_GATE_UP = 1
@@ -209,6 +211,21 @@ def smoe_expert_layout_of(d_model: int, ffn_dim: int, bits: int,
     _check(load_library().smoe_expert_layout_of(d_model, ffn_dim, bits, scale_dtype,
                                                  ctypes.byref(out)))
     return out
+
+
+def aligned_buffer(nbytes: int, device="cuda:0", align: int = SMOE_BANK_ALIGN,
+                   pin_memory: bool = False):
+    """A uint8 torch tensor of nbytes whose data starts on an `align` boundary
+    (expert banks and shared blobs must be 16 KB aligned): a view into an
+    allocation `align` bytes larger, which the view keeps alive. With
+    pin_memory the buffer is pinned host memory, else device memory."""
+    import torch
+    if pin_memory:
+        base = torch.empty(nbytes + align, dtype=torch.uint8, pin_memory=True)
+    else:
+        base = torch.empty(nbytes + align, dtype=torch.uint8, device=device)
+    off = (-base.data_ptr()) % align
+    return base[off: off + nbytes]
 
 
 def make_desc(d_model: int, ffn_dim: int, num_experts: int, bits: int,

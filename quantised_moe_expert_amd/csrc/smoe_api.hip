@@ -10,6 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -23,13 +24,6 @@ namespace smoe {
 namespace {
 
 thread_local char g_err[512] = "";
-
-// Set from the environment at load: SMOE_FORCE_MULTI_KERNEL=1 makes batch-1
-// calls take the multi-kernel path (used to test both paths).
-const bool g_force_multi = [] {
-  const char* v = getenv("SMOE_FORCE_MULTI_KERNEL");
-  return v && v[0] == '1';
-}();
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -94,6 +88,12 @@ int make_plan(uint32_t d, uint32_t ffn, uint32_t bits, uint32_t sdt, ExpertPlan*
       return fail(SMOE_E_UNSUPPORTED,
                   "no kernel for a [%u, %u] Q%u tensor (row of %u code words)", t[i]->rows,
                   t[i]->cols, bits, t[i]->cols * bits / 32);
+  // the batched stages stage each token (x as fp32 hi + lo for the residual
+  // stream) or each h row in one four-wave workgroup's 64 KB of LDS
+  if (!batch_fits(P->gate, true) || !batch_fits(P->down, false))
+    return fail(SMOE_E_UNSUPPORTED,
+                "d_model %u / ffn_dim %u: one activation vector does not fit the batched "
+                "stages' 64 KB staging", d, ffn);
   if (Lout) *Lout = L;
   return SMOE_OK;
 }
@@ -130,9 +130,10 @@ WsLayout ws_layout(const LayerInfo& L, int T, int k) {
   return W;
 }
 
-// armed timing events (smoe_trace_kernel)
+// armed timing events (smoe_trace_kernel); the kernel id is read without the
+// lock, so a forward takes no lock while nothing is armed
 std::mutex g_trace_mu;
-int g_trace_kernel = SMOE_KERNEL_NONE;
+std::atomic<int> g_trace_kernel{SMOE_KERNEL_NONE};
 hipEvent_t g_trace_before = nullptr, g_trace_after = nullptr;
 
 int check_hip(hipError_t e, const char* what) {
@@ -141,11 +142,14 @@ int check_hip(hipError_t e, const char* what) {
 }
 
 // The shared expert's stream and fork / join events, created on first use
-// (on the current device) so that registering a layer needs no GPU.
+// (on the current device) so that registering a layer needs no GPU. The
+// events are the layer's own: a forward holds g_side_mu from the fork until
+// its stream has queued the wait on the join, so that calls from several
+// threads never re-record an event between another call's record and wait.
 std::mutex g_side_mu;
 
+// g_side_mu held
 hipError_t side_stream(const LayerInfo& L) {
-  std::lock_guard<std::mutex> lock(g_side_mu);
   if (L.side) return hipSuccess;
   hipStream_t st = nullptr;
   hipEvent_t f = nullptr, j = nullptr;
@@ -165,10 +169,12 @@ hipError_t side_stream(const LayerInfo& L) {
 }
 
 // One layer: route+group, gate/up+SwiGLU, down, combine (optionally into the
-// residual stream with RMSNorm applied on the way in).
+// residual stream with RMSNorm applied on the way in). side_ok: the shared
+// expert may run on the layer's side stream (else on s, before routing).
 int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const float* logits,
                  int T, int k, int norm, float* out, int accumulate, int32_t* uids, float* uw,
-                 uint8_t* ws, hipStream_t s, const RouteCfg& cfg = RouteCfg()) {
+                 uint8_t* ws, hipStream_t s, const RouteCfg& cfg = RouteCfg(),
+                 bool side_ok = true) {
   const WsLayout W = ws_layout(L, T, k);
   int32_t* ids = (int32_t*)(ws + W.ids);
   float* w = (float*)(ws + W.w);
@@ -182,7 +188,7 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
   const int E = (int)L.desc.num_experts;
   const int max_slots = T * k < E ? T * k : E;
   int rc;
-  if (T == 1 && !g_force_multi && cfg.is_default()) {
+  if (T == 1 && cfg.is_default()) {
     bool launched = false;
     if ((rc = check_hip(decode1_try(L, x, xmode != X_BF16, xmode == X_F32_RMS, eps, logits, k,
                                     norm, out, accumulate, uids, uw, h, ids, w, s, &launched),
@@ -194,22 +200,28 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
   // the work enqueued so far, beside routing and the routed stages, and the
   // combine waits for it
   float* ysh = nullptr;
+  std::unique_lock<std::mutex> side_lock;
   if (L.desc.shared_ffn_dim) {
     float* hsh = (float*)(ws + W.h_shared);
     ysh = (float*)(ws + W.y_shared);
-    if ((rc = check_hip(side_stream(L), "shared-expert stream and events")) ||
-        (rc = check_hip(hipEventRecord(L.fork, s), "shared-expert fork")) ||
-        (rc = check_hip(hipStreamWaitEvent(L.side, L.fork, 0), "shared-expert fork")))
-      return rc;
+    hipStream_t ss = s;
+    if (side_ok) {
+      side_lock = std::unique_lock<std::mutex>(g_side_mu);
+      if ((rc = check_hip(side_stream(L), "shared-expert stream and events")) ||
+          (rc = check_hip(hipEventRecord(L.fork, s), "shared-expert fork")) ||
+          (rc = check_hip(hipStreamWaitEvent(L.side, L.fork, 0), "shared-expert fork")))
+        return rc;
+      ss = L.side;
+    }
     if ((rc = check_hip(launch_gate_up(L, true, x, xmode, eps, T, T, 1, meta, active, offs,
-                                       pair_token, hsh, L.side, nullptr),
+                                       pair_token, hsh, ss, nullptr),
                         "shared gate/up launch")))
       return rc;
-    if ((rc = check_hip(launch_down(L, true, hsh, T, T, 1, meta, active, offs, ysh, L.side,
+    if ((rc = check_hip(launch_down(L, true, hsh, T, T, 1, meta, active, offs, ysh, ss,
                                     nullptr),
                         "shared down launch")))
       return rc;
-    if ((rc = check_hip(hipEventRecord(L.join, L.side), "shared-expert join")))
+    if (side_ok && (rc = check_hip(hipEventRecord(L.join, L.side), "shared-expert join")))
       return rc;
   }
   if ((rc = check_hip(launch_route(logits, T, E, k, norm, ids, w, uids, uw, 1, meta, active,
@@ -230,8 +242,10 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
                    "down launch");
   }
   if (rc) return rc;
-  if (ysh && (rc = check_hip(hipStreamWaitEvent(s, L.join, 0), "shared-expert join")))
-    return rc;
+  if (side_lock.owns_lock()) {
+    if ((rc = check_hip(hipStreamWaitEvent(s, L.join, 0), "shared-expert join"))) return rc;
+    side_lock.unlock();
+  }
   return check_hip(
       launch_combine(y, pair_of, w, ysh, cfg.shared_gate, out, T, k, (int)L.desc.d_model,
                      accumulate, s),
@@ -253,11 +267,12 @@ int report_ok() { return ok(); }
 thread_local LaunchEvents t_launch_events;
 
 bool trace_take(int kernel, hipEvent_t* start, hipEvent_t* stop) {
+  if (g_trace_kernel.load(std::memory_order_acquire) != kernel) return false;
   std::lock_guard<std::mutex> lk(g_trace_mu);
-  if (g_trace_kernel != kernel) return false;
+  if (g_trace_kernel.load(std::memory_order_relaxed) != kernel) return false;
   *start = g_trace_before;
   *stop = g_trace_after;
-  g_trace_kernel = SMOE_KERNEL_NONE;
+  g_trace_kernel.store(SMOE_KERNEL_NONE, std::memory_order_release);
   return true;
 }
 
@@ -413,8 +428,7 @@ int smoe_route_ex(const float* d_logits, int n_tokens, int n_experts, int top_k,
   return rc ? rc : ok();
 }
 
-static int check_forward_args(const smoe_layer* layer, int n_tokens, int top_k,
-                              const void* d_workspace, uint64_t ws_bytes) {
+static int check_layer_args(const smoe_layer* layer, int n_tokens, int top_k) {
   if (!layer) return fail(SMOE_E_ARG, "null layer");
   if (n_tokens < 0 || n_tokens > SMOE_MAX_TOKENS)
     return fail(SMOE_E_ARG, "n_tokens must be in [0, %d] (got %d)", SMOE_MAX_TOKENS, n_tokens);
@@ -425,7 +439,13 @@ static int check_forward_args(const smoe_layer* layer, int n_tokens, int top_k,
   if (!group_fits(E, n_tokens))
     return fail(SMOE_E_UNSUPPORTED, "%d tokens over %d experts exceed the grouping's LDS", n_tokens,
                 E);
-  if (n_tokens == 0) return SMOE_OK;
+  return SMOE_OK;
+}
+
+static int check_forward_args(const smoe_layer* layer, int n_tokens, int top_k,
+                              const void* d_workspace, uint64_t ws_bytes) {
+  const int rc = check_layer_args(layer, n_tokens, top_k);
+  if (rc || n_tokens == 0) return rc;
   const uint64_t need = ws_layout(layer->info, n_tokens, top_k).total;
   if (!d_workspace || ws_bytes < need)
     return fail(SMOE_E_WORKSPACE, "workspace of %llu bytes needed (got %llu)",
@@ -516,10 +536,10 @@ int smoe_trace_kernel(int kernel, void* hip_event_before, void* hip_event_after)
   if (kernel != SMOE_KERNEL_NONE && (!hip_event_before || !hip_event_after))
     return fail(SMOE_E_ARG, "null event");
   std::lock_guard<std::mutex> lk(g_trace_mu);
-  const int pending = g_trace_kernel != SMOE_KERNEL_NONE ? 1 : 0;
-  g_trace_kernel = kernel;
+  const int pending = g_trace_kernel.load(std::memory_order_relaxed) != SMOE_KERNEL_NONE ? 1 : 0;
   g_trace_before = (hipEvent_t)hip_event_before;
   g_trace_after = (hipEvent_t)hip_event_after;
+  g_trace_kernel.store(kernel, std::memory_order_release);
   return kernel == SMOE_KERNEL_NONE ? pending : SMOE_OK;
 }
 

@@ -95,12 +95,8 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(D
   // units per batch; two batches are in flight (double buffering). More
   // loads in flight per wave measured slower: the first batch then arrives
   // later and the memory queues hold more concurrent row streams.
-#ifdef SMOE_DEC_UB
-  constexpr int UB = SMOE_DEC_UB;
-#else
   constexpr int UBr = (SPLIT ? 36 : 24) / (2 * (VG + SPG::NS));
   constexpr int UB = UBr < 1 ? 1 : (UBr > 4 ? 4 : UBr);
-#endif
   constexpr int XP = VG * PPW * 64;
   constexpr int XRAW = XF32 ? WPW : WPW / 2;  // 32-bit words of x per code word
 
@@ -362,12 +358,8 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(Deco
   constexpr int NPOS = QT<BITS>::NPOS;
   using SPD = ScalePlan<BITS, VD>;
   // row loads per batch, two batches in flight
-#ifdef SMOE_DEC_UD
-  constexpr int UD = SMOE_DEC_UD;
-#else
   constexpr int UDr = 32 / (VD + SPD::NS);
   constexpr int UD = UDr < 1 ? 1 : (UDr > 8 ? 8 : UDr);
-#endif
 
   __shared__ float s_part[SMOE_MAX_TOP_K * DEC_RB_MAX];
 

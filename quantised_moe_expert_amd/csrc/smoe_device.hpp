@@ -367,4 +367,33 @@ __device__ __forceinline__ float lane_row(const uint32_t (&cw)[V], const XRegs<B
   return acc;
 }
 
+// The WPW activations of code word cw of vector v (bf16 or fp32 elements).
+template <int BITS, bool XF32>
+__device__ __forceinline__ void gv_load_word(const void* v, int cw, float (&xv)[QT<BITS>::WPW]) {
+  constexpr int WPW = QT<BITS>::WPW;
+  if constexpr (XF32) {
+    const float* p = (const float*)v + (size_t)cw * WPW;
+#pragma unroll
+    for (int i = 0; i < WPW / 4; ++i) {
+      const f32x4 t = *(const f32x4*)(p + 4 * i);
+      xv[4 * i] = t.x;
+      xv[4 * i + 1] = t.y;
+      xv[4 * i + 2] = t.z;
+      xv[4 * i + 3] = t.w;
+    }
+  } else {
+    const uint32_t* p = (const uint32_t*)v + (size_t)cw * (WPW / 2);
+#pragma unroll
+    for (int i = 0; i < WPW / 8; ++i) {
+      const u32x4 t = *(const u32x4*)(p + 4 * i);
+      const uint32_t tt[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xv[8 * i + 2 * j] = __builtin_bit_cast(float, tt[j] << 16);
+        xv[8 * i + 2 * j + 1] = __builtin_bit_cast(float, tt[j] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
 }  // namespace smoe

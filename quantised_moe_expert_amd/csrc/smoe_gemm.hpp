@@ -29,16 +29,13 @@
 #include <type_traits>
 
 #include "smoe_device.hpp"
-#include "smoe_gemv.hpp"
 #include "smoe_gemv_args.hpp"
 #include "smoe_launch.hpp"
 
-#ifndef SMOE_GM_GB
-#define SMOE_GM_GB 8
-#endif
-
-
 namespace smoe {
+
+// scale groups per weight load batch (a multiple of 4)
+constexpr int GM_GB = 8;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f32x4m __attribute__((ext_vector_type(4)));
@@ -235,7 +232,7 @@ template <int BITS, typename ST, int IN, bool GU, bool SV, int NW>
 __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) void k_gemm(GemvArgs A) {
   extern __shared__ uint32_t lds[];
   constexpr int WPG = QT<BITS>::WPG, HALVES = QT<BITS>::PPW / 4;
-  constexpr int GB = SMOE_GM_GB;  // groups per load batch (multiple of 4)
+  constexpr int GB = GM_GB;
   static_assert(GB % 4 == 0, "batches start at multiples of four groups");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -1,4 +1,4 @@
-// Argument block of the expert GEMV stages (shared by the dispatcher and
+// Argument block of the batched expert stages (shared by the dispatcher and
 // the kernel instantiation units).
 #pragma once
 
@@ -7,36 +7,8 @@
 
 namespace smoe {
 
-// Words-per-lane values with a kernel instantiation (each row of W code words
-// is spread over W / V lanes, a power of two <= 64).
-#define SMOE_V_LIST(X) \
-  X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
-
-// Grouped stages: 4-wave workgroups (see smoe_gemv.hpp).
-constexpr int GV_THREADS = 256;
-constexpr int GV_WAVES = GV_THREADS / 64;
-
 // Activation forms of the staged vectors.
 enum GvIn { GV_BF16 = 0, GV_F32_SPLIT = 1, GV_F32 = 2 };
-
-// LDS layout of one chunk (in 32-bit words): hi pairs [TC][cols/2], lo pairs
-// [TC][cols/2] (split only), K [TC][NK * LPR], output scale [TC], and the
-// per-wave statistics [TC][GV_WAVES][2].
-struct GvLds {
-  int xhi, xlo, k, osc, red, total;
-};
-
-__host__ __device__ inline GvLds gv_lds_layout(int cols, int lpr, int nk, int tc, bool split) {
-  GvLds L;
-  const int xs = cols / 2;
-  L.xhi = 0;
-  L.xlo = tc * xs;
-  L.k = L.xlo + (split ? tc * xs : 0);
-  L.osc = L.k + tc * nk * lpr;
-  L.red = L.osc + tc;
-  L.total = L.red + tc * GV_WAVES * 2;
-  return L;
-}
 
 // LDS layout of the matrix-core stage (32-bit words) for a workgroup of nw
 // waves: token pairs [TC * cols / 2] (+ the same again for the lo halves of
@@ -121,13 +93,6 @@ struct GemvArgs {
   const float* prep_k;
   const float* prep_o;
 };
-
-// Launchers, defined in smoe_gemv.hpp and instantiated per (BITS, scale
-// type, V) by the smoe_gemv_inst.hip units.
-template <int BITS, typename ST, int V>
-hipError_t launch_gu(const GemvArgs& A, int in, dim3 grid, unsigned lds, hipStream_t s);
-template <int BITS, typename ST, int V>
-hipError_t launch_dn(const GemvArgs& A, dim3 grid, unsigned lds, hipStream_t s);
 
 // Matrix-core stage launchers (smoe_gemm.hpp, instantiated per (BITS, scale
 // type) by smoe_gemm_inst.hip); in: GvIn of the activations.

@@ -36,6 +36,11 @@ struct ExpertPlan {
 bool plan_matrix(int rows, int cols, int bits, uint64_t codes_off, uint64_t scales_off,
                  MatPlan* out);
 
+// Whether the batched stages can stage one activation vector of this
+// matrix's input width (fp32 split into hi + lo halves when split) in the
+// 64 KB of LDS of a four-wave workgroup.
+bool batch_fits(const MatPlan& m, bool split);
+
 // Workspace layout of one forward (offsets in bytes from the workspace base).
 struct WsLayout {
   uint64_t ids, w, meta, active, offs, pair_token, pair_of;

@@ -74,6 +74,45 @@ def tiny_swiglu_layer(seed: int = 0):
     return x, HostLayer(256, 128, 1, 4, "f32", 0, blob, L.padded_size, None)
 
 
+def to_device_aligned(host: np.ndarray, device="cuda:0", pin_memory: bool = False):
+    """Bytes of `host` in a 16 KB-aligned device (or pinned host) buffer, as
+    the library requires for expert banks and shared blobs."""
+    import torch
+    import quantised_moe_expert_amd as smoe
+    buf = smoe.aligned_buffer(host.size, device=device, pin_memory=pin_memory)
+    buf.copy_(torch.from_numpy(np.ascontiguousarray(host).reshape(-1)))
+    return buf
+
+
+def oracle_by_expert(ol: O.OracleLayer, x: np.ndarray, logits: np.ndarray, k: int,
+                     norm: bool):
+    """The oracle's layer output for every token, evaluated expert by expert:
+    each selected expert is dequantised once, into three reused arrays, and
+    applied to every token routed to it, so a batch over many experts never
+    holds more than one dense expert. Same terms as O.moe_forward,
+    out[t] = sum_j w[t, j] FFN_{ids[t, j]}(x[t]) (+ the shared expert with
+    weight 1); only the order of the per-token sum differs."""
+    T = x.shape[0]
+    X = np.asarray(x, np.float64)
+    routes = [O.route(logits[t], k, norm) for t in range(T)]
+    by_e = {}
+    for t, (ids, _) in enumerate(routes):
+        for j, e in enumerate(ids):
+            by_e.setdefault(e, []).append((t, j))
+    out = np.zeros((T, ol.d_model))
+    bufs = {n: np.empty(sp.rows * sp.cols, np.float64) for n, sp in ol.layout.spans().items()}
+    for e in sorted(by_e):
+        W = ol.expert_weights_into(e, bufs)
+        for t, j in by_e[e]:
+            out[t] += routes[t][1][j] * O.swiglu_expert(W["gate"], W["up"], W["down"], X[t])
+    S = ol.shared_weights()
+    if S is not None:
+        for t in range(T):
+            out[t] += O.swiglu_expert(S["gate"], S["up"], S["down"], X[t])
+        ol.drop_cache()
+    return out, routes
+
+
 def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
@@ -90,11 +129,11 @@ class DeviceLayer:
         self.hl = hl
         self.smoe = smoe
         self.bank = bank_tensor if bank_tensor is not None else \
-            torch.from_numpy(hl.bank).to(device)
+            to_device_aligned(hl.bank, device)
         self.shared = None
         if hl.shared_blob is not None:
             self.shared = shared_tensor if shared_tensor is not None else \
-                torch.from_numpy(hl.shared_blob).to(device)
+                to_device_aligned(hl.shared_blob, device)
         desc = smoe.make_desc(hl.d, hl.ffn, hl.E, hl.bits, hl.stride, SCALE_CODE[hl.scale_dtype],
                               hl.shared_ffn)
         self.handle = smoe.smoe_load_blobs(

@@ -106,8 +106,14 @@ def test_grouping_that_does_not_fit_lds_is_unsupported():
     (dict(blob_stride=10_616_832 + 64), 0, FAKE, smoe.SMOE_E_LAYOUT),
     (dict(), -1, FAKE, smoe.SMOE_E_LAYOUT),
     (dict(), 0, FAKE + 16, smoe.SMOE_E_LAYOUT),
+    # banks start on the 16 KB page boundary (".smoe Binary Format", Immutable
+    # Encoding): a 256-byte-aligned base is refused
+    (dict(), 0, FAKE + 256, smoe.SMOE_E_LAYOUT),
+    (dict(), 0, FAKE + 8192, smoe.SMOE_E_LAYOUT),
     (dict(), 0, 0, smoe.SMOE_E_ARG),
-    (dict(d_model=64 * 17), 0, FAKE, smoe.SMOE_E_UNSUPPORTED),
+    # one fp32 token (hi + lo pairs, offsets, k-split partial sums) of width
+    # 12800 exceeds the batched stages' 64 KB staging
+    (dict(d_model=64 * 200), 0, FAKE, smoe.SMOE_E_UNSUPPORTED),
 ])
 def test_load_blobs_validation(kw, nbytes_delta, ptr, code):
     desc = _desc(**kw)
@@ -117,6 +123,38 @@ def test_load_blobs_validation(kw, nbytes_delta, ptr, code):
         smoe.smoe_load_blobs(desc, ptr, nbytes)
     assert e.value.code == code
     assert smoe.smoe_last_error()
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("d,ffn,ok", [(11392, 1536, True), (11456, 1536, False),
+                                      (4096, 19072, True), (4096, 19136, False)])
+def test_activation_width_limits_at_load(bits, d, ffn, ok):
+    # the batched stages stage one fp32 token as hi + lo fp16 pairs plus
+    # offsets and partial sums (1.25 d + 2072 words), one h row as pairs
+    # (0.75 ffn + 2072 words), in 16384 words of LDS
+    st = O.expert_layout(d, ffn, bits).padded_size
+    desc = smoe.make_desc(d, ffn, 2, bits, st)
+    if ok:
+        smoe.smoe_free(smoe.smoe_load_blobs(desc, FAKE, 2 * st))
+        return
+    with pytest.raises(smoe.SmoeError) as e:
+        smoe.smoe_load_blobs(desc, FAKE, 2 * st)
+    assert e.value.code == smoe.SMOE_E_UNSUPPORTED
+
+
+def test_shared_blob_alignment_and_width():
+    SL = O.expert_layout(2048, 2816, 4)
+    st = O.expert_layout(2048, 1408, 4).padded_size
+    desc = smoe.make_desc(2048, 1408, 64, 4, st, shared_ffn_dim=2816)
+    for off in (256, 8192):
+        with pytest.raises(smoe.SmoeError) as e:
+            smoe.smoe_load_blobs(desc, FAKE, 64 * st, FAKE + off, SL.raw_size)
+        assert e.value.code == smoe.SMOE_E_LAYOUT
+    wide = smoe.make_desc(2048, 1408, 64, 4, st, shared_ffn_dim=19136)
+    with pytest.raises(smoe.SmoeError) as e:
+        smoe.smoe_load_blobs(wide, FAKE, 64 * st, FAKE,
+                             O.expert_layout(2048, 19136, 4).raw_size)
+    assert e.value.code == smoe.SMOE_E_UNSUPPORTED
 
 
 def test_load_blobs_exact_minimum_size_is_enough():

@@ -11,7 +11,7 @@ import pytest
 
 import oracle as O
 import synth
-from helpers import DeviceLayer, random_layer, rel_l2, tiny_swiglu_layer
+from helpers import DeviceLayer, oracle_by_expert, random_layer, rel_l2, tiny_swiglu_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -125,6 +125,18 @@ def test_small_layers(case, x_dtype):
     x = _x(r, T, d, x_dtype)
     lg = synth.normal_f32(r, (T, E))
     _check_layer(hl, x, lg, k, norm, x_dtype)
+
+
+# the widest activation vectors the library registers (wider ones are
+# refused at load): one token, and batches through the grouped stages
+@pytest.mark.parametrize("d,ffn,shared", [(11392, 128, 0), (128, 19072, 19072)])
+@pytest.mark.parametrize("T", [1, 3])
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_maximum_widths(d, ffn, shared, T, x_dtype):
+    _torch()
+    hl = random_layer(70 + d + T, d, ffn, 4, 4, "f16", shared)
+    r = synth.rng(71 + T)
+    _check_layer(hl, _x(r, T, d, x_dtype), synth.normal_f32(r, (T, 4)), 2, True, x_dtype)
 
 
 def test_stride_larger_than_padded_blob():
@@ -307,14 +319,25 @@ def test_qwen235b_q4_b1_full():
 
 
 @pytest.mark.parametrize("name", ["qwen235b_q4_b32", "qwen235b_q2_b32"])
-def test_qwen235b_b32_sampled(name):
+def test_qwen235b_b32_every_token(name):
+    # "CMF v2 Format Specification", 2.2 MoE: out[t] = sum_j w_j FFN_j(x[t])
+    # for each of the 32 tokens (about 112 distinct experts, each dequantised
+    # once by the oracle and applied to all of its tokens)
     _torch()
     W = synth.WORKLOADS[name]
     hl = random_layer(W.seed + W.bits, W.d_model, W.ffn_dim, W.num_experts, W.bits)
     r = synth.rng(W.seed + 2000)
     x = _x(r, W.n_tokens, W.d_model, "bf16")
     lg = synth.normal_f32(r, (W.n_tokens, W.num_experts))
-    _check_layer(hl, x, lg, W.top_k, W.norm_topk_prob, "bf16", tokens=[0, 13, 31])
+    print(f"{name}: all {W.n_tokens} tokens", flush=True)
+    out, ids, w = DeviceLayer(hl).forward(x, lg, W.top_k, W.norm_topk_prob, "bf16")
+    ref, routes = oracle_by_expert(hl.oracle(), x, lg, W.top_k, W.norm_topk_prob)
+    for t, (want, wt) in enumerate(routes):
+        assert ids[t].tolist() == want, (t, ids[t], want)
+        assert np.allclose(w[t], wt, rtol=1e-5, atol=1e-7)
+    assert np.all(np.isfinite(out))
+    per_tok = [rel_l2(out[t], ref[t]) for t in range(W.n_tokens)]
+    assert rel_l2(out, ref) <= TOL and max(per_tok) <= TOL, (rel_l2(out, ref), max(per_tok))
 
 
 # Prefill-sized batches: 32 pairs per expert fill whole 16-token chunks; with
@@ -415,3 +438,48 @@ def test_qwen_stack_three_layers_full_width():
     ref = O.decode_step([h.oracle() for h in hls], x, list(lg), W.top_k, True, 1e-6)
     assert rel_l2(got, ref) <= TOL
     assert rel_l2(got - x, ref - x) <= TOL   # the accumulated MoE delta
+
+
+def test_qwen_stack_94_layers_full_width():
+    # the 94 MoE layers of the Qwen3-235B shape ("SMOE Quantisation", Why
+    # Quantise), d 4096, ffn 1536, Q4, RMSNorm eps 1e-6 (".smoe Binary Format",
+    # Arch Block), one token, distinct logits per layer. To fit the oracle's
+    # time and memory the layers alternate over two banks of 8 experts
+    # (top-8: every expert of the layer's bank is selected, in the order and
+    # with the weights of that layer's logits); the oracle dequantises each
+    # of the 16 experts once. Checked on h and on the accumulated MoE delta h - x, so
+    # an error that grows with depth shows.
+    torch = _torch()
+    import quantised_moe_expert_amd as smoe
+    W = synth.WORKLOADS["qwen235b_q4_stack94"]
+    nl, nb, E, k = 94, 2, 8, 8
+    print(f"stack: {nl} layers over {nb} banks of {E} experts", flush=True)
+    hls = [random_layer(W.seed * 1000 + b, W.d_model, W.ffn_dim, E, W.bits) for b in range(nb)]
+    r = synth.rng(W.seed + 9400)
+    x = synth.normal_f32(r, (1, W.d_model))
+    lg = synth.normal_f32(r, (nl, 1, E))
+    dls = [DeviceLayer(h) for h in hls]
+    h_d = torch.from_numpy(x.copy()).cuda()
+    lg_d = torch.from_numpy(lg).cuda()
+    nws = smoe.smoe_workspace_bytes(dls[0].handle, 1, k)
+    ws = torch.zeros(nws, dtype=torch.uint8, device="cuda")
+    smoe.smoe_decode_step([dls[l % nb].handle for l in range(nl)], h_d.data_ptr(),
+                          lg_d.data_ptr(), 1, k, True, 1e-6, ws.data_ptr(), nws, 0)
+    torch.cuda.synchronize()
+    got = h_d.cpu().numpy().astype(np.float64)
+    # oracle: h = x; per layer h += MoE_l(rms_norm(h)), each bank's experts
+    # dequantised once
+    ols = [h.oracle() for h in hls]
+    dense = [{e: ol.expert_weights(e) for e in range(E)} for ol in ols]
+    h = x.astype(np.float64)
+    for l in range(nl):
+        n = O.rms_norm(h, 1e-6)[0]
+        ids, w = O.route(lg[l, 0], k, True)
+        y = np.zeros(W.d_model)
+        for j, e in enumerate(ids):
+            D = dense[l % nb][e]
+            y += w[j] * O.swiglu_expert(D["gate"], D["up"], D["down"], n)
+        h = h + y
+    err_h, err_d = rel_l2(got, h), rel_l2(got - x, h - x)
+    print(f"stack: rel L2 h {err_h:.2e}, delta {err_d:.2e}", flush=True)
+    assert err_h <= TOL and err_d <= TOL
