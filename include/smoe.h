@@ -252,6 +252,34 @@ int smoe_moe_forward_ex(const smoe_layer* layer, const void* d_x, int x_dtype,
                         float* d_topk_w, void* d_workspace, uint64_t ws_bytes,
                         void* hip_stream);
 
+/* Device bytes of the static scratch behind smoe_moe_forward_noalloc, per
+ * GPU. */
+#define SMOE_NOALLOC_SCRATCH_BYTES (32ull << 20)
+
+/* smoe_moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same computation and results, with two differences: the workspace is a
+ * static array of SMOE_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends, and the shared expert runs on
+ * hip_stream itself, before routing (no side stream or events).
+ *  Arguments as smoe_moe_forward without d_workspace and ws_bytes;
+ *  hip_stream (NULL: the null stream) belongs to the current device.
+ * Calls no hipMalloc, hipFree or other allocating routine; the first call on
+ * a device looks up that device's copy of the array (hipGetSymbolAddress).
+ * Every call on one GPU uses that GPU's one array, which keeps the previous
+ * call's contents (each call writes every word it reads, so nothing needs
+ * clearing): calls that overlap on one GPU (several streams, or threads
+ * without ordering between them) race and give wrong results.
+ * Errors: those of smoe_moe_forward, SMOE_E_WORKSPACE when
+ * smoe_workspace_bytes(layer, n_tokens, top_k) exceeds
+ * SMOE_NOALLOC_SCRATCH_BYTES (e.g. past 186 tokens at top-8 for experts of
+ * (4096, 1536), past 279 at top-6 for (2048, 1408) with a (2048, 2816) shared
+ * expert), SMOE_E_HIP. n_tokens == 0 is a no-op. */
+int smoe_moe_forward_noalloc(const smoe_layer* layer, const void* d_x, int x_dtype,
+                             const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
+                             float* d_out, int32_t* d_topk_ids, float* d_topk_w,
+                             void* hip_stream);
+
 /* Stacked decode step over n_layers MoE layers (same d_model):
  *   for l in 0..n_layers-1:  h = h + MoE_l(rms_norm(h, eps))
  * with unit-gain RMSNorm n = h / sqrt(mean(h^2) + eps) per token.

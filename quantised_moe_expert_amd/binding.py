@@ -33,6 +33,7 @@ SMOE_SCALE_F16 = 1
 SMOE_MAX_TOP_K = 16
 SMOE_MAX_EXPERTS = 512
 SMOE_MAX_TOKENS = 4096
+SMOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 SMOE_MAX_QUANT_ELEMENTS = 1 << 31
 SMOE_BLOB_ALIGN = 16384
 SMOE_BANK_ALIGN = 16384
@@ -46,7 +47,7 @@ EXPORTED = (
     "smoe_version", "smoe_last_error", "smoe_expert_layout_of", "smoe_load_blobs",
     "smoe_free", "smoe_workspace_bytes", "smoe_route", "smoe_moe_forward",
     "smoe_decode_step", "smoe_trace_kernel", "smoe_route_opts_init", "smoe_route_ex",
-    "smoe_moe_forward_ex", "smoe_quantise",
+    "smoe_moe_forward_ex", "smoe_quantise", "smoe_moe_forward_noalloc",
     # include/smoe_vault.h
     "smoe_arch_block_init", "smoe_vault_plan", "smoe_vault_create", "smoe_vault_put_expert",
     "smoe_vault_finish", "smoe_vault_open", "smoe_vault_close", "smoe_vault_get_header",
@@ -183,6 +184,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.smoe_moe_forward_ex.argtypes = [_P, _P, _I, _P, _I, _I, _I,
                                         ctypes.POINTER(smoe_route_opts), _P, _P, _P, _P, _U64,
                                         _P]
+    lib.smoe_moe_forward_noalloc.restype = _I
+    lib.smoe_moe_forward_noalloc.argtypes = [_P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _P]
     from .vault import declare as _declare_vault
     from .offload import declare as _declare_offload
     _declare_vault(lib)
@@ -287,6 +290,15 @@ def smoe_moe_forward_ex(layer: int, d_x: int, x_dtype: int, d_logits: int, n_tok
         layer, d_x or None, x_dtype, d_logits or None, n_tokens, top_k,
         int(bool(norm_topk_prob)), ctypes.byref(opts) if opts is not None else None,
         d_out or None, d_topk_ids or None, d_topk_w or None, d_workspace or None, ws_bytes,
+        hip_stream or None))
+
+
+def smoe_moe_forward_noalloc(layer: int, d_x: int, x_dtype: int, d_logits: int,
+                             n_tokens: int, top_k: int, norm_topk_prob: bool, d_out: int,
+                             d_topk_ids: int, d_topk_w: int, hip_stream: int = 0) -> None:
+    _check(load_library().smoe_moe_forward_noalloc(
+        layer, d_x or None, x_dtype, d_logits or None, n_tokens, top_k,
+        int(bool(norm_topk_prob)), d_out or None, d_topk_ids or None, d_topk_w or None,
         hip_stream or None))
 
 

@@ -485,6 +485,66 @@ int smoe_moe_forward_ex(const smoe_layer* layer, const void* d_x, int x_dtype,
   return rc ? rc : ok();
 }
 
+// Workspace of smoe_moe_forward_noalloc: one array per GPU, allocated with
+// the library's code object when it is loaded on that GPU and held until the
+// process ends. Host code never passes the array's name to a kernel (on the
+// host it is a stand-in, not a device address): the address comes from
+// hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[SMOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`.
+int scratch_for_current_device(uint8_t** out) {
+  int dev = -1;
+  int rc = check_hip(hipGetDevice(&dev), "current device");
+  if (rc) return rc;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SMOE_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if ((rc = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address")))
+      return rc;
+    if (!p || !aligned(p, 256)) return fail(SMOE_E_HIP, "scratch address %p is not usable", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (uint8_t*)g_scratch_ptr[dev];
+  return SMOE_OK;
+}
+}  // namespace
+
+int smoe_moe_forward_noalloc(const smoe_layer* layer, const void* d_x, int x_dtype,
+                             const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
+                             float* d_out, int32_t* d_topk_ids, float* d_topk_w,
+                             void* hip_stream) {
+  int rc = check_layer_args(layer, n_tokens, top_k);
+  if (rc) return rc;
+  if (x_dtype != SMOE_DTYPE_BF16 && x_dtype != SMOE_DTYPE_F32)
+    return fail(SMOE_E_ARG, "x_dtype must be SMOE_DTYPE_BF16 or SMOE_DTYPE_F32");
+  if (n_tokens == 0) return ok();
+  const uint64_t need = ws_layout(layer->info, n_tokens, top_k).total;
+  if (need > SMOE_NOALLOC_SCRATCH_BYTES)
+    return fail(SMOE_E_WORKSPACE,
+                "%d tokens at top-%d need %llu bytes of workspace; the static scratch holds "
+                "%llu (use smoe_moe_forward with a workspace of that size)",
+                n_tokens, top_k, (unsigned long long)need,
+                (unsigned long long)SMOE_NOALLOC_SCRATCH_BYTES);
+  if (!d_x || !d_logits || !d_out) return fail(SMOE_E_ARG, "null x, logits or out");
+  if (!aligned(d_x, 16)) return fail(SMOE_E_ARG, "x must be 16-byte aligned");
+  if (!aligned(d_logits, 4) || !aligned(d_out, 4))
+    return fail(SMOE_E_ARG, "logits and out must be 4-byte aligned");
+  uint8_t* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws))) return rc;
+  rc = forward_impl(layer->info, d_x, x_dtype == SMOE_DTYPE_BF16 ? X_BF16 : X_F32, 0.f,
+                    d_logits, n_tokens, top_k, norm_topk_prob != 0, d_out, 0, d_topk_ids,
+                    d_topk_w, ws, (hipStream_t)hip_stream, RouteCfg(), /*side_ok=*/false);
+  return rc ? rc : ok();
+}
+
 int smoe_decode_step(const smoe_layer* const* layers, int n_layers, float* d_h,
                      const float* d_logits, int n_tokens, int top_k, int norm_topk_prob,
                      float eps, void* d_workspace, uint64_t ws_bytes, void* hip_stream) {

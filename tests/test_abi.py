@@ -211,6 +211,36 @@ def test_forward_argument_checks_before_any_launch():
         smoe.smoe_free(h)
 
 
+def test_noalloc_argument_checks_before_any_launch():
+    # every case is refused (or is a no-op) before the library looks up its
+    # scratch or touches a device
+    desc = _desc()
+    h = smoe.smoe_load_blobs(desc, FAKE, 128 * desc.blob_stride)
+    try:
+        ok = dict(layer=h, d_x=FAKE, x_dtype=smoe.SMOE_DTYPE_BF16, d_logits=FAKE, n_tokens=1,
+                  top_k=8, norm_topk_prob=True, d_out=FAKE, d_topk_ids=0, d_topk_w=0)
+        assert smoe.smoe_workspace_bytes(h, 186, 8) <= smoe.SMOE_NOALLOC_SCRATCH_BYTES
+        assert smoe.smoe_workspace_bytes(h, 187, 8) > smoe.SMOE_NOALLOC_SCRATCH_BYTES
+        cases = [
+            (dict(n_tokens=187), smoe.SMOE_E_WORKSPACE),
+            (dict(n_tokens=smoe.SMOE_MAX_TOKENS), smoe.SMOE_E_WORKSPACE),
+            (dict(n_tokens=smoe.SMOE_MAX_TOKENS + 1), smoe.SMOE_E_ARG),
+            (dict(n_tokens=-1), smoe.SMOE_E_ARG),
+            (dict(top_k=0), smoe.SMOE_E_ARG), (dict(top_k=17), smoe.SMOE_E_ARG),
+            (dict(x_dtype=5), smoe.SMOE_E_ARG), (dict(d_x=0), smoe.SMOE_E_ARG),
+            (dict(d_out=0), smoe.SMOE_E_ARG), (dict(d_logits=0), smoe.SMOE_E_ARG),
+            (dict(d_x=FAKE + 2), smoe.SMOE_E_ARG), (dict(d_out=FAKE + 2), smoe.SMOE_E_ARG),
+            (dict(layer=0), smoe.SMOE_E_ARG),
+        ]
+        for over, code in cases:
+            with pytest.raises(smoe.SmoeError) as e:
+                smoe.smoe_moe_forward_noalloc(**dict(ok, **over))
+            assert e.value.code == code, over
+        smoe.smoe_moe_forward_noalloc(**dict(ok, n_tokens=0, d_x=0, d_out=0))  # no-op
+    finally:
+        smoe.smoe_free(h)
+
+
 def test_route_and_decode_argument_checks():
     with pytest.raises(smoe.SmoeError):
         smoe.smoe_route(FAKE, 1, 128, 17, True, FAKE, FAKE)
