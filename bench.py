@@ -299,6 +299,28 @@ def main():
                                "algorithmic_bytes_per_launch": int(v["bytes"]),
                                "GBps": round(v["GBps"], 1)} for n, v in kern.items()},
     }
+    if dom and args.trace_launches > 0:
+        sizes = [int(dom["bytes"]), int(alg_bytes)]
+        if "down" in kern:
+            sizes.append(int(kern["down"]["bytes"]))
+        ceil = stream_ceiling(sizes, args.trace_launches)
+        c_gu = ceil[sizes[0] // 16 * 16]
+        c_step = ceil[sizes[1] // 16 * 16]
+        sc = {
+            "method": "libsmoe_stream.so read kernel, event pair per launch, best of "
+                      "normal/non-temporal loads x 256-2048 workgroups, windows rotated "
+                      "over 2 GiB",
+            "gate_up_bytes": sizes[0], "gate_up_us": round(c_gu, 3),
+            "step_bytes_one_launch": sizes[1], "step_one_launch_us": round(c_step, 3),
+        }
+        result["roofline"]["stream_ceiling_us"] = round(c_gu, 3)
+        result["roofline"]["pct_of_stream_ceiling"] = round(100 * c_gu / dom["mean_us"], 2)
+        if "down" in kern:
+            c_dn = ceil[sizes[2] // 16 * 16]
+            sc.update(down_bytes=sizes[2], down_us=round(c_dn, 3),
+                      down_pct_of_stream_ceiling=round(100 * c_dn / kern["down"]["mean_us"], 2))
+        result["stream_ceiling"] = sc
+        result["pct_of_stream_ceiling"] = round(100 * c_step / (ms * 1e3), 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, W, banks[0], stride, lg_sets[0, 0], x,
                                               shared_blobs[0] if shared_blobs else None)
@@ -569,6 +591,53 @@ def committed_traffic(workload: str, kernel: str):
     return None
 
 
+def stream_ceiling(sizes, trace_n):
+    """Streaming-read ceiling for each byte count in `sizes`: the mean launch
+    time of libsmoe_stream.so's plain read kernel over that many bytes, timed
+    exactly as the layer kernels are (an event pair around each launch on the
+    launch stream), the best over normal / non-temporal loads and 256 to 2048
+    workgroups. Every launch reads a different window of a 2 GiB buffer, so
+    nothing is served from the 256 MB Infinity Cache. Returns {bytes: us}."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "quantised_moe_expert_amd", "libsmoe_stream.so"))
+    lib.smoe_stream_read.restype = ctypes.c_int
+    lib.smoe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    pool = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    n = max(trace_n, 20)
+    out = {}
+    for nbytes in sizes:
+        nbytes = int(nbytes) // 16 * 16
+        span = (nbytes + 16383) // 16384 * 16384
+        windows = (pool.numel() - span) // span
+        best = None
+        for nt in (0, 1):
+            for nwg in (256, 512, 1024, 2048):
+                evs = [(torch.cuda.Event(enable_timing=True),
+                        torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+                for j in range(-8, n):  # eight untimed launches first
+                    src = pool.data_ptr() + (j % windows) * span
+                    if j >= 0:
+                        evs[j][0].record(stream)
+                    rc = lib.smoe_stream_read(src, nbytes, sink.data_ptr(), nwg, nt,
+                                              stream.cuda_stream)
+                    if rc:
+                        raise RuntimeError(f"smoe_stream_read failed ({rc})")
+                    if j >= 0:
+                        evs[j][1].record(stream)
+                torch.cuda.synchronize()
+                us = sum(a.elapsed_time(b) for a, b in evs) / n * 1e3
+                if best is None or us < best:
+                    best = us
+        out[nbytes] = best
+    del pool
+    return out
+
+
 def copy_calibration():
     """A plain device-to-device copy of 1 GiB, five times: under rocprofv3
     --pmc its FETCH_SIZE / WRITE_SIZE per dispatch, divided by 1 GiB, are the
@@ -586,10 +655,11 @@ def copy_calibration():
 def cpu_baseline(args, W, bank, stride, logits, x, shared_blob):
     """The oracle, as it stands, on host cores: repeated single-layer forwards
     of the same workload (tokens of the first logit set, first bank copy) for
-    about --cpu-baseline-seconds."""
+    about --cpu-baseline-seconds with every core the BLAS pool uses, then as
+    long again on one thread."""
     import numpy as np
     import oracle as O
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     lg = logits.float().cpu().numpy()
     xs = x.float().cpu().numpy()
@@ -600,21 +670,25 @@ def cpu_baseline(args, W, bank, stride, logits, x, shared_blob):
     sh = shared_blob.cpu().numpy() if shared_blob is not None else None
     layer = O.OracleLayer(W.d_model, W.ffn_dim, W.num_experts, W.bits, None, stride,
                           "f32", W.shared_ffn_dim, sh, expert_blobs=blobs)
-    t0 = time.perf_counter()
-    n_tok = 0
-    reps = 0
-    while True:
-        layer.drop_cache()
-        for t in range(T):
-            O.moe_forward(layer, xs[t:t + 1], lg[t:t + 1], k, W.norm_topk_prob)
-            n_tok += 1
+
+    def leg():
+        t0 = time.perf_counter()
+        n_tok = 0
+        while True:
+            layer.drop_cache()
+            for t in range(T):
+                O.moe_forward(layer, xs[t:t + 1], lg[t:t + 1], k, W.norm_topk_prob)
+                n_tok += 1
+                if time.perf_counter() - t0 > args.cpu_baseline_seconds:
+                    break
             if time.perf_counter() - t0 > args.cpu_baseline_seconds:
                 break
-        reps += 1
-        if time.perf_counter() - t0 > args.cpu_baseline_seconds:
-            break
-    dt = time.perf_counter() - t0
+        return n_tok, time.perf_counter() - t0
+
+    n_tok, dt = leg()
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    with threadpool_limits(limits=1):
+        n1, dt1 = leg()
     return {
         "value": round(n_tok / dt, 4),
         "unit": "tokens/s",
@@ -623,6 +697,9 @@ def cpu_baseline(args, W, bank, stride, logits, x, shared_blob):
         "sample": (f"{n_tok} token forwards of one {W.name} layer (experts dequantised "
                    f"from the blob bytes per forward), {dt:.1f} s, "
                    f"host cpu_count={os.cpu_count()}"),
+        "single_thread": {"value": round(n1 / dt1, 4), "unit": "tokens/s", "cores": 1,
+                          "sample": f"{n1} token forwards, {dt1:.1f} s, BLAS pool limited "
+                                    "to one thread"},
     }
 
 
