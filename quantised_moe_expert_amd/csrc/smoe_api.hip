@@ -98,9 +98,25 @@ int make_plan(uint32_t d, uint32_t ffn, uint32_t bits, uint32_t sdt, ExpertPlan*
   return SMOE_OK;
 }
 
+// The shared expert runs inside the routed launches, as nsh = shared_ffn /
+// ffn more slots over all T tokens, when its ffn is a multiple of the routed
+// one (at most 16 times) and the launches take the plain matrix-core stages
+// (the K-sliced prefill stages run routed slots only); then the result is
+// nsh, else 0 and the shared expert has launches of its own.
+int shared_parts(const LayerInfo& L, int T, int k) {
+  const uint32_t sf = L.desc.shared_ffn_dim, f = L.desc.ffn_dim;
+  if (!sf || sf % f || sf / f > 16) return 0;
+  const int nsh = (int)(sf / f);
+  const int P = T * k, E = (int)L.desc.num_experts;
+  if (gmk_wanted(P + nsh * T, (P < E ? P : E) + nsh)) return 0;
+  return nsh;
+}
+
 WsLayout ws_layout(const LayerInfo& L, int T, int k) {
   WsLayout W{};
   const uint64_t P = (uint64_t)T * k, E = L.desc.num_experts;
+  const uint64_t nsh = (uint64_t)shared_parts(L, T, k);
+  const uint64_t PT = P + nsh * T;  // pairs, the shared expert's parts included
   uint64_t o = 0;
   auto take = [&](uint64_t bytes) {
     const uint64_t at = o;
@@ -111,13 +127,13 @@ WsLayout ws_layout(const LayerInfo& L, int T, int k) {
   W.w = take(P * 4);
   W.meta = take(64);
   W.active = take(E * 4);
-  W.offs = take((E + 1) * 4);
-  W.pair_token = take(P * 4);
+  W.offs = take((E + 1 + nsh) * 4);
+  W.pair_token = take(PT * 4);
   W.pair_of = take(P * 4);
-  W.h = take(P * L.desc.ffn_dim * 4);
-  W.y = take(P * L.desc.d_model * 4);
-  W.h_shared = take((uint64_t)T * L.desc.shared_ffn_dim * 4);
-  W.y_shared = take(L.desc.shared_ffn_dim ? (uint64_t)T * L.desc.d_model * 4 : 0);
+  W.h = take(PT * L.desc.ffn_dim * 4);
+  W.y = take(PT * L.desc.d_model * 4);
+  W.h_shared = take(nsh ? 0 : (uint64_t)T * L.desc.shared_ffn_dim * 4);
+  W.y_shared = take(!nsh && L.desc.shared_ffn_dim ? (uint64_t)T * L.desc.d_model * 4 : 0);
   const uint64_t slots = P < E ? P : E;
   W.prep_bytes = 0;
   if (gmk_wanted((int)P, (int)slots)) {
@@ -187,6 +203,8 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
   float* y = (float*)(ws + W.y);
   const int E = (int)L.desc.num_experts;
   const int max_slots = T * k < E ? T * k : E;
+  const int nsh = shared_parts(L, T, k);
+  const int pairs = T * k + nsh * T;
   int rc;
   if (T == 1 && cfg.is_default()) {
     bool launched = false;
@@ -199,9 +217,9 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
   // the shared expert needs only x: it runs on the layer's side stream from
   // the work enqueued so far, beside routing and the routed stages, and the
   // combine waits for it
-  float* ysh = nullptr;
+  float* ysh = nsh ? y + (size_t)T * k * L.desc.d_model : nullptr;
   std::unique_lock<std::mutex> side_lock;
-  if (L.desc.shared_ffn_dim) {
+  if (L.desc.shared_ffn_dim && !nsh) {
     float* hsh = (float*)(ws + W.h_shared);
     ysh = (float*)(ws + W.y_shared);
     hipStream_t ss = s;
@@ -225,20 +243,21 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
       return rc;
   }
   if ((rc = check_hip(launch_route(logits, T, E, k, norm, ids, w, uids, uw, 1, meta, active,
-                                   offs, pair_token, pair_of, s, cfg),
+                                   offs, pair_token, pair_of, s, cfg, nsh),
                       "route launch")))
     return rc;
+  void* prep = W.prep_bytes && !nsh ? ws + W.prep : nullptr;
   {
     TracedLaunch t(SMOE_KERNEL_GATE_UP);
-    rc = check_hip(launch_gate_up(L, false, x, xmode, eps, T, T * k, max_slots, meta, active, offs,
-                                  pair_token, h, s, W.prep_bytes ? ws + W.prep : nullptr),
+    rc = check_hip(launch_gate_up(L, false, x, xmode, eps, T, pairs, max_slots, meta, active, offs,
+                                  pair_token, h, s, prep, nsh),
                    "gate/up launch");
   }
   if (rc) return rc;
   {
     TracedLaunch t(SMOE_KERNEL_DOWN);
-    rc = check_hip(launch_down(L, false, h, T, T * k, max_slots, meta, active, offs, y, s,
-                               W.prep_bytes ? ws + W.prep : nullptr),
+    rc = check_hip(launch_down(L, false, h, T, pairs, max_slots, meta, active, offs, y, s, prep,
+                               nsh),
                    "down launch");
   }
   if (rc) return rc;
@@ -247,7 +266,8 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
     side_lock.unlock();
   }
   return check_hip(
-      launch_combine(y, pair_of, w, ysh, cfg.shared_gate, out, T, k, (int)L.desc.d_model,
+      launch_combine(y, pair_of, w, ysh, nsh ? nsh : 1, cfg.shared_gate, out, T, k,
+                     (int)L.desc.d_model,
                      accumulate, s),
       "combine launch");
 }

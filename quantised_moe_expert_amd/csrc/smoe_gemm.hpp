@@ -236,20 +236,45 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
   static_assert(GB % 4 == 0, "batches start at multiples of four groups");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int e = 0, p0, p1;
+  const MatArgs& M0 = A.m0;
+  const int rows = M0.rows, Wr = M0.words_per_row, G = M0.cols / 64, TC = A.tc;
+  // the slot's pairs, matrices and row pitch (words, groups)
+  int p0, p1, rpw = Wr, rpg = G;
+  const uint8_t* blob;
+  uint64_t c0off = M0.codes_off, s0off = M0.scales_off;
+  uint64_t c1off = A.m1.codes_off, s1off = A.m1.scales_off;
   if (A.shared) {
     p0 = 0;
     p1 = A.T;
+    blob = A.blobs;
   } else {
-    const int slot = blockIdx.y;
-    if (slot >= A.meta[0]) return;  // workgroup-uniform
-    e = A.active[slot];
+    const int slot = blockIdx.y, nr = A.meta[0];
+    if (slot >= nr + A.nsh) return;  // workgroup-uniform
     p0 = A.offs[slot];
     p1 = A.offs[slot + 1];
+    if (slot < nr) {
+      blob = expert_blob(A.blobs, A.stride, A.table, A.active[slot]);
+    } else {
+      // part v of the shared expert: a block of its gate/up rows, or a block
+      // of its down columns (rows nsh times as long)
+      const uint64_t v = (uint64_t)(slot - nr);
+      blob = A.sh_blob;
+      if constexpr (GU) {
+        c0off = A.sh_m0.codes_off + v * rows * Wr * 4;
+        s0off = A.sh_m0.scales_off + v * rows * G * sizeof(ST);
+        c1off = A.sh_m1.codes_off + v * rows * Wr * 4;
+        s1off = A.sh_m1.scales_off + v * rows * G * sizeof(ST);
+      } else {
+        c0off = A.sh_m0.codes_off + v * Wr * 4;
+        s0off = A.sh_m0.scales_off + v * G * sizeof(ST);
+        c1off = c0off;
+        s1off = s0off;
+        rpw = A.nsh * Wr;
+        rpg = A.nsh * G;
+      }
+    }
   }
   if (p0 >= p1) return;  // workgroup-uniform
-  const MatArgs& M0 = A.m0;
-  const int rows = M0.rows, Wr = M0.words_per_row, G = M0.cols / 64, TC = A.tc;
   const int ks = A.ksplit;           // waves per 16-row tile: 1 or 4 (4 only with NW = 4)
   const int tpw = A.tiles_per_wave;  // tiles a wave takes in turn (1 with the k-split)
   const int tw = wave / ks, kpart = wave - tw * ks;
@@ -258,11 +283,10 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
   const int gb0 = min(G, kpart * gper), gb1 = min(G, gb0 + gper);
   const int nbt = (gb1 - gb0 + GB - 1) / GB;  // batches per tile (0: an empty k-part)
   const int nb = nbt * tpw;                   // batches of this wave per chunk
-  const uint8_t* blob = expert_blob(A.blobs, A.stride, A.table, e);
-  const uint32_t* cm0 = (const uint32_t*)(blob + M0.codes_off);
-  const ST* sm0 = (const ST*)(blob + M0.scales_off);
-  const uint32_t* cm1 = (const uint32_t*)(blob + A.m1.codes_off);
-  const ST* sm1 = (const ST*)(blob + A.m1.scales_off);
+  const uint32_t* cm0 = (const uint32_t*)(blob + c0off);
+  const ST* sm0 = (const ST*)(blob + s0off);
+  const uint32_t* cm1 = (const uint32_t*)(blob + c1off);
+  const ST* sm1 = (const ST*)(blob + s1off);
   constexpr bool SPLIT = IN == GV_F32_SPLIT;
   const GmLds L = gm_lds_layout(M0.cols, TC, SPLIT, NW);
   const uint32_t* X = lds + L.x;
@@ -305,10 +329,10 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
   auto load = [&](Batch& B, int k) {
     const Pos P = pos(k);
     const int rc = min(row_of(P.t), rows - 1);
-    const uint32_t* c0 = cm0 + (size_t)rc * Wr;
-    const uint32_t* c1 = cm1 + (size_t)rc * Wr;
-    const ST* s0 = sm0 + (size_t)rc * G;
-    const ST* s1 = sm1 + (size_t)rc * G;
+    const uint32_t* c0 = cm0 + (size_t)rc * rpw;
+    const uint32_t* c1 = cm1 + (size_t)rc * rpw;
+    const ST* s0 = sm0 + (size_t)rc * rpg;
+    const ST* s1 = sm1 + (size_t)rc * rpg;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       B.wa[u] = gm_unit_load<BITS>(c0, P.g0 + u * UG, G, b);

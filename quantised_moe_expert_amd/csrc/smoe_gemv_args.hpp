@@ -87,6 +87,14 @@ struct GemvArgs {
   const int* offs;
   const int* pair_token;
   float* out;            // gate/up: h [pairs, rows]; down: y [pairs, rows]
+  // A shared expert whose ffn is nsh times the routed one, run in the same
+  // launch as nsh more slots after the routed ones: slot (routed count) + v
+  // takes rows [v * rows, (v + 1) * rows) of its gate and up matrices
+  // (sh_m0, sh_m1), or columns [v * cols, (v + 1) * cols) of its down matrix
+  // (sh_m0), over all T tokens. nsh = 0: routed slots only.
+  const uint8_t* sh_blob;
+  int nsh;
+  MatArgs sh_m0, sh_m1;
   // K-sliced stage: activation vectors prepared by k_gmk_prep (fp16 pair
   // quads [V][cols / 8], group offsets [V][cols / 64], output factors [V])
   const uint32_t* prep_x;

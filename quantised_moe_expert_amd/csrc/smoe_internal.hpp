@@ -104,21 +104,24 @@ struct RouteCfg {
 hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int32_t* ids,
                         float* w, int32_t* user_ids, float* user_w, int group, int* meta,
                         int* active, int* offs, int* pair_token, int* pair_of,
-                        hipStream_t stream, const RouteCfg& cfg = RouteCfg());
+                        hipStream_t stream, const RouteCfg& cfg = RouteCfg(), int nsh = 0);
 
-// pairs: routed (token, expert) pairs of the call (T for the shared expert),
-// used to size the launch.
+// pairs: (token, expert) pairs of the launch (T for the shared expert on its
+// own; routed plus nsh * T with the shared expert fused), used to size it.
 // prep: workspace for prepared activations (gmk_prep_bytes of the stage), or
 // null when the call has none.
+// nsh > 0: the shared expert runs in the same launch as nsh slots after the
+// routed ones (its ffn is nsh times the routed ffn; see GemvArgs), reading
+// pairs P + v * T + t (P = routed pairs) of h and writing those rows of y.
 hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xmode,
                           float rms_eps, int T, int pairs, int max_slots, const int* meta,
                           const int* active, const int* offs, const int* pair_token,
-                          float* h, hipStream_t stream, void* prep);
+                          float* h, hipStream_t stream, void* prep, int nsh = 0);
 
 hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int pairs,
                        int max_slots,
                        const int* meta, const int* active, const int* offs, float* y,
-                       hipStream_t stream, void* prep);
+                       hipStream_t stream, void* prep, int nsh = 0);
 
 // Batch-1 path (two launches); sets *launched = false (and enqueues nothing)
 // when the layer's shape has no instantiation.
@@ -127,11 +130,12 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
                        int32_t* uids, float* uw, float* h, int32_t* ws_ids, float* ws_w,
                        hipStream_t stream, bool* launched);
 
-// shared_gate (nullable, [T] logits): the shared expert's weight is
+// y_shared (nullable): nsh partial outputs of the shared expert, [nsh][T][d],
+// summed; shared_gate (nullable, [T] logits): the shared expert's weight is
 // sigmoid(shared_gate[t]) instead of 1.
 hipError_t launch_combine(const float* y, const int* pair_of, const float* w,
-                          const float* y_shared, const float* shared_gate, float* out, int T,
-                          int k, int d, int accumulate, hipStream_t stream);
+                          const float* y_shared, int nsh, const float* shared_gate, float* out,
+                          int T, int k, int d, int accumulate, hipStream_t stream);
 
 // Group-64 squared-error scale search + encode + pack of n fp32 weights
 // (flattened order; a short last group is allowed).

@@ -33,6 +33,7 @@ struct RouteArgs {
   int* offs;
   int* pair_token;
   int* pair_of;
+  int nsh;  // shared-expert slots appended after the routed ones (T pairs each)
 };
 
 // Selection key of expert e with logit f: unsigned order of the keys is the
@@ -341,11 +342,13 @@ __global__ __launch_bounds__(GROUP_THREADS) void k_group(RouteArgs A) {
       npairs += __shfl(ic, 63, 64);
     }
     if (lane == 0) {
-      A.offs[nact] = npairs;
+      for (int v = 0; v <= A.nsh; ++v) A.offs[nact + v] = npairs + v * A.T;
       A.meta[0] = nact;
       A.meta[1] = npairs;
     }
   }
+  // the shared-expert slots: pair P + v * T + t is token t
+  for (int i = tid; i < A.nsh * A.T; i += blockDim.x) A.pair_token[P + i] = i % A.T;
   __syncthreads();
   // pair (t, j): its rank among the expert's tokens is the tokens before its
   // word's block, plus the words of the block before its word, plus the bits
@@ -367,9 +370,9 @@ __global__ __launch_bounds__(GROUP_THREADS) void k_group(RouteArgs A) {
 hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int32_t* ids,
                         float* w, int32_t* user_ids, float* user_w, int group, int* meta,
                         int* active, int* offs, int* pair_token, int* pair_of,
-                        hipStream_t stream, const RouteCfg& cfg) {
+                        hipStream_t stream, const RouteCfg& cfg, int nsh) {
   RouteArgs A{logits, T, E, k, norm, group, cfg, ids, w, user_ids, user_w,
-              meta, active, offs, pair_token, pair_of};
+              meta, active, offs, pair_token, pair_of, nsh};
   const int tpb = TOPK_THREADS / 64;
   int blocks = (T + tpb - 1) / tpb;
   blocks = blocks > 1024 ? 1024 : blocks;
@@ -394,7 +397,9 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int norm, int3
 }
 
 // ---------------------------------------------------------------- combine --
-// out[t, i] (+)= sum_j w[t, j] * y[pair_of[t, j], i] + y_shared[t, i]
+// out[t, i] (+)= sum_j w[t, j] * y[pair_of[t, j], i] + g_t * sum_v y_shared[v * T + t, i]
+// (nsh partial outputs of the shared expert, summed in v order; g_t = 1, or
+// the sigmoid of the token's shared-gate logit)
 
 constexpr int COMBINE_THREADS = 128;
 
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void k_combine(const float* __rest
                                                              const float* __restrict__ y_shared,
                                                              const float* __restrict__ shared_gate,
                                                              float* __restrict__ out, int k, int d,
-                                                             int accumulate) {
+                                                             int accumulate, int nsh, int T) {
   using V = float __attribute__((ext_vector_type(VEC)));
   const int t = blockIdx.y;
   const int i = (blockIdx.x * COMBINE_THREADS + threadIdx.x) * VEC;
@@ -421,7 +426,12 @@ __global__ __launch_bounds__(COMBINE_THREADS) void k_combine(const float* __rest
     for (int c = 0; c < VEC; ++c) acc[c] = fmaf(wj, yv[c], acc[c]);
   }
   if (y_shared) {
-    const V ys = *(const V*)(y_shared + (size_t)t * d + i);
+    V ys = *(const V*)(y_shared + (size_t)t * d + i);
+    for (int v = 1; v < nsh; ++v) {
+      const V yv = *(const V*)(y_shared + ((size_t)v * T + t) * d + i);
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) ys[c] += yv[c];
+    }
     const float den = shared_gate ? 1.0f + expf(-shared_gate[t]) : 1.0f;
 #pragma unroll
     for (int c = 0; c < VEC; ++c) acc[c] += shared_gate ? ys[c] / den : ys[c];
@@ -436,17 +446,17 @@ __global__ __launch_bounds__(COMBINE_THREADS) void k_combine(const float* __rest
 }
 
 hipError_t launch_combine(const float* y, const int* pair_of, const float* w,
-                          const float* y_shared, const float* shared_gate, float* out, int T,
-                          int k, int d, int accumulate, hipStream_t stream) {
+                          const float* y_shared, int nsh, const float* shared_gate, float* out,
+                          int T, int k, int d, int accumulate, hipStream_t stream) {
   // y and y_shared are workspace rows (256-byte aligned, d a multiple of 64)
   if (((uintptr_t)out & 15) == 0 && d % 4 == 0) {
     dim3 grid((d + 4 * COMBINE_THREADS - 1) / (4 * COMBINE_THREADS), T);
     hipLaunchKernelGGL(k_combine<4>, grid, dim3(COMBINE_THREADS), 0, stream, y, pair_of, w,
-                       y_shared, shared_gate, out, k, d, accumulate);
+                       y_shared, shared_gate, out, k, d, accumulate, nsh, T);
   } else {
     dim3 grid((d + COMBINE_THREADS - 1) / COMBINE_THREADS, T);
     hipLaunchKernelGGL(k_combine<1>, grid, dim3(COMBINE_THREADS), 0, stream, y, pair_of, w,
-                       y_shared, shared_gate, out, k, d, accumulate);
+                       y_shared, shared_gate, out, k, d, accumulate, nsh, T);
   }
   return hipGetLastError();
 }
@@ -661,7 +671,7 @@ static hipError_t gmk_dispatch(const LayerInfo& L, GemvArgs& A, bool gate_up, co
 hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xmode,
                           float rms_eps, int T, int pairs, int max_slots, const int* meta,
                           const int* active, const int* offs, const int* pair_token,
-                          float* h, hipStream_t stream, void* prep) {
+                          float* h, hipStream_t stream, void* prep, int nsh) {
   const ExpertPlan& P = shared ? L.shared_plan : L.plan;
   GemvArgs A{};
   A.blobs = shared ? L.shared : L.blobs;
@@ -680,13 +690,19 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
   A.offs = offs;
   A.pair_token = pair_token;
   A.out = h;
+  if (nsh > 0) {
+    A.sh_blob = L.shared;
+    A.nsh = nsh;
+    A.sh_m0 = mat_args(L.shared_plan.gate);
+    A.sh_m1 = mat_args(L.shared_plan.up);
+  }
   const int in = xmode == X_BF16 ? GV_BF16 : GV_F32_SPLIT;
-  if (prep && !shared && in == GV_BF16 && gmk_wanted(pairs, max_slots))
+  if (prep && !shared && nsh == 0 && in == GV_BF16 && gmk_wanted(pairs, max_slots))
     return gmk_dispatch(L, A, true, x, false, T, P.gate.rows, P.d_model, max_slots, prep, stream);
   dim3 grid;
   unsigned lds;
   int nw;
-  if (gm_shape(P.gate, in == GV_F32_SPLIT, pairs, shared ? 1 : max_slots, A, grid, lds, nw))
+  if (gm_shape(P.gate, in == GV_F32_SPLIT, pairs, shared ? 1 : max_slots + nsh, A, grid, lds, nw))
     return L.desc.scale_dtype == SMOE_SCALE_F32
                ? gm_dispatch<float>(L.desc.bits, A, true, in, nw, grid, lds, stream)
                : gm_dispatch<_Float16>(L.desc.bits, A, true, in, nw, grid, lds, stream);
@@ -697,7 +713,7 @@ hipError_t launch_gate_up(const LayerInfo& L, bool shared, const void* x, int xm
 hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, int pairs,
                        int max_slots,
                        const int* meta, const int* active, const int* offs, float* y,
-                       hipStream_t stream, void* prep) {
+                       hipStream_t stream, void* prep, int nsh) {
   const ExpertPlan& P = shared ? L.shared_plan : L.plan;
   GemvArgs A{};
   A.blobs = shared ? L.shared : L.blobs;
@@ -713,12 +729,18 @@ hipError_t launch_down(const LayerInfo& L, bool shared, const float* h, int T, i
   A.active = active;
   A.offs = offs;
   A.out = y;
-  if (prep && !shared && gmk_wanted(pairs, max_slots))
+  if (nsh > 0) {
+    A.sh_blob = L.shared;
+    A.nsh = nsh;
+    A.sh_m0 = mat_args(L.shared_plan.down);
+    A.sh_m1 = A.sh_m0;
+  }
+  if (prep && !shared && nsh == 0 && gmk_wanted(pairs, max_slots))
     return gmk_dispatch(L, A, false, h, true, pairs, P.down.rows, P.ffn, max_slots, prep, stream);
   dim3 grid;
   unsigned lds;
   int nw;
-  if (gm_shape(P.down, false, pairs, shared ? 1 : max_slots, A, grid, lds, nw))
+  if (gm_shape(P.down, false, pairs, shared ? 1 : max_slots + nsh, A, grid, lds, nw))
     return L.desc.scale_dtype == SMOE_SCALE_F32
                ? gm_dispatch<float>(L.desc.bits, A, false, GV_F32, nw, grid, lds, stream)
                : gm_dispatch<_Float16>(L.desc.bits, A, false, GV_F32, nw, grid, lds, stream);

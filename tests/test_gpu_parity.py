@@ -100,6 +100,11 @@ SMALL = [
     (2048, 1408, 4, 2, 2, 4, "f32", False, 2816),
     (2048, 1408, 6, 3, 3, 2, "f16", True, 2816),
     (640, 448, 12, 5, 7, 4, "f32", True, 0),
+    # shared experts 4x and 3x the routed ffn (run as extra slots of the
+    # routed launches) and one that is not a multiple (launches of its own)
+    (512, 320, 16, 4, 5, 4, "f16", True, 1280),
+    (640, 448, 12, 5, 7, 2, "f32", False, 1344),
+    (512, 320, 16, 4, 6, 4, "f32", True, 448),
     # one token: the single-launch path for these widths ...
     (512, 320, 16, 4, 1, 4, "f32", True, 0),
     (512, 320, 16, 4, 1, 2, "f16", False, 0),
