@@ -188,7 +188,19 @@ def main():
     x_bytes = T * W.d_model * (2 if W.x_dtype == "bf16" else 4)
     gu_raw = sum(t.codes_bytes + t.scales_bytes for t in (lay.gate, lay.up))
     dn_raw = lay.down.codes_bytes + lay.down.scales_bytes
-    h_bytes = T * k * W.ffn_dim * 4
+    # a shared expert whose ffn is a multiple of the routed ffn runs inside the
+    # routed launches (as shared_ffn / ffn more slots of all T tokens) unless
+    # the call takes the K-sliced stages (24 or more pairs per slot on average)
+    nsh, sh_gu, sh_dn = 0, 0, 0
+    if W.shared_ffn_dim and W.shared_ffn_dim % W.ffn_dim == 0:
+        q = W.shared_ffn_dim // W.ffn_dim
+        if q <= 16 and (T * k + q * T) // (min(T * k, E) + q) < 24:
+            nsh = q
+            sl = smoe.smoe_expert_layout_of(W.d_model, W.shared_ffn_dim, W.bits,
+                                            smoe.SMOE_SCALE_F32)
+            sh_gu = sum(t.codes_bytes + t.scales_bytes for t in (sl.gate, sl.up))
+            sh_dn = sl.down.codes_bytes + sl.down.scales_bytes
+    h_bytes = (T * k + nsh * T) * W.ffn_dim * 4
     start = args.warmup + args.steps
     # does this layer have a separate down-projection launch?
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -222,10 +234,11 @@ def main():
             dts = [a.elapsed_time(b) * 1e-3 for a, b in evs]  # s
             u = [uniq0[(start + i) % n_logit_sets] for i in range(n)]
             if name == "gate_up":
-                byts = [ui * gu_raw + x_bytes + T * E * 4 + h_bytes for ui in u]
+                byts = [ui * gu_raw + sh_gu + x_bytes + T * E * 4 + h_bytes for ui in u]
             else:
                 byts = [ui * dn_raw + h_bytes + out_b if single else
-                        ui * dn_raw + h_bytes + T * k * W.d_model * 4 for ui in u]
+                        ui * dn_raw + sh_dn + h_bytes + (T * k + nsh * T) * W.d_model * 4
+                        for ui in u]
             mean_dt = sum(dts) / n
             mean_b = sum(byts) / n
             kern[name] = {"mean_us": mean_dt * 1e6, "median_us": sorted(dts)[n // 2] * 1e6,
@@ -241,7 +254,7 @@ def main():
     traffic = committed_traffic(W.name, "gate_up" if single else "gate_up_grouped")
     # the gate/up launch's contraction: two flops per weight per routed pair
     # (one layer per launch); the roofline is whichever peak bounds it first
-    gu_flops = T * k * 4 * W.d_model * W.ffn_dim
+    gu_flops = (T * k + nsh * T) * 4 * W.d_model * W.ffn_dim
     roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": None}
     if dom:
         dt = dom["mean_us"] * 1e-6
@@ -606,7 +619,8 @@ def stream_ceiling(sizes, trace_n):
                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    pool = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    big = max(int(b) for b in sizes)
+    pool = torch.ones(max(2 << 30, 4 * big + (1 << 20)), dtype=torch.uint8, device=dev)
     sink = torch.empty(65536, dtype=torch.int32, device=dev)
     n = max(trace_n, 20)
     out = {}
