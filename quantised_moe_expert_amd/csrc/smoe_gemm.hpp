@@ -531,39 +531,46 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
 //
 // For slots with many tokens (prefill-sized batches) each weight fetch
 // should serve more tokens than one MFMA's 16, but a 4096-wide token vector
-// takes 8 KB of LDS as fp16, so 64 tokens do not fit whole. This stage takes
-// the chunk's 64 tokens one K slice (eight scale groups, 512 weights) at a
-// time into one of two LDS buffers and feeds every decoded weight operand to
-// four MFMA token tiles, so a slot's weights are read once per 64 tokens
-// instead of once per 16.
+// takes 8 KB of LDS as fp16, so a chunk of 64 or 128 tokens does not fit
+// whole. This stage takes the chunk one K slice (four scale groups, 256
+// weights) at a time into one of two LDS buffers and feeds every decoded
+// weight operand to NTT MFMA token tiles, so a slot's weights are read once
+// per chunk.
 //   - The token vectors were converted beforehand (k_gmk_prep) into the
 //     fp16 pairs, group offsets K and output factors of k_gemm's staging,
 //     stored per vector in the order of the MFMA operand, so a slice is
 //     copied global -> LDS with direct-to-LDS loads (global_load_lds_dwordx4:
 //     lane i writes 16 bytes at LDS base + 16 i), no registers and no
-//     conversion in this kernel. One load moves one token's slice (a
-//     contiguous kilobyte, 8 cache lines); token rows in LDS are one quad
-//     longer than the slice, so the 16 tokens an MFMA operand read touches
-//     sit on distinct banks.
-//   - Each wave owns one 16-row tile of one matrix: for gate/up, waves 0-3
-//     take four gate tiles and waves 4-7 the up tiles of the same 64 rows
-//     (their results meet in LDS for SwiGLU); for down, eight tiles.
-//   - Per slice: the next slice's weights, then its tokens (into the other
-//     buffer), are loaded before the current slice is multiplied; a wait for
-//     all of the wave's loads and one barrier end the slice.
+//     conversion in this kernel. Such a load costs the CU about 48 cycles of
+//     issue whatever its size, so each one moves a whole kilobyte (two
+//     tokens' 512-byte slices) and they are spread one per scale group over
+//     the slice being multiplied. In LDS a pair's row is 66 quads long and
+//     the odd token's quads are rotated by one, so the 16 tokens an MFMA
+//     operand read touches sit on 16 different bank quads.
+//   - Each wave owns two 16-row tiles: for gate/up the gate and the up rows
+//     of the same 16 rows (SwiGLU is then applied in registers), for down
+//     two adjacent tiles. Each token operand read from LDS feeds both tiles.
+//   - Per slice: the next slice's weights (registers) and tokens (the other
+//     LDS buffer) are requested before the current slice is multiplied; one
+//     wait for the wave's loads and one barrier end the slice.
+//   - A slot's tokens are cut into chunks of nearly equal size; token rows
+//     past the chunk's end read stale LDS rows, whose sums are dropped.
+//   - Within a group the LDS operands of tile t + 1 are read while tile t is
+//     multiplied, and tile t - 1's sums are scaled after tile t's MFMAs are
+//     issued, so no vector instruction waits on an MFMA it just issued.
 
-template <int BITS, typename ST, bool GU, bool SV>
+template <int BITS, typename ST, bool GU, bool SV, int NTT>
 __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
   extern __shared__ uint32_t lds[];
   constexpr int WPG = QT<BITS>::WPG, HALVES = QT<BITS>::PPW / 4;
-  // two 16-row tiles per wave where the scales come as vector quads; one
-  // otherwise (per-group scale registers would not fit beside two tiles)
-  constexpr int TC = GMK_TC, NTT = TC / 16, KSG = GMK_KSG, GB = KSG, TPW = gmk_tpw(SV);
-  static_assert(TC == 64, "one direct-to-LDS load per token per lane");
-  constexpr int QPS = KSG * WPG * HALVES;  // 16-byte pair quads of a slice per token
-  static_assert(QPS == 64, "a slice is 512 weights");
-  static_assert(GMK_XTS == (QPS + 1) * 4, "token rows of one slice and a padding quad");
-  constexpr int XB = TC * GMK_XTS, KB = KSG * TC;
+  constexpr int TC = 16 * NTT, KSG = GMK_KSG, QPS = GMK_QPS, XPS = GMK_XPS;
+  static_assert(KSG * WPG * HALVES == QPS, "a slice is KSG groups of 8 pair quads");
+  constexpr int XB = TC / 2 * XPS * 4, KB = KSG * TC;
+  constexpr int TPW = GMK_TPW;
+  constexpr int UG = BITS == 4 ? 2 : 4;  // scale groups per 16-byte unit load
+  constexpr int NU = KSG / UG;
+  constexpr int PPV = TC / 2 / GMK_NW;   // token pairs each wave copies per slice
+  static_assert(QPS == 32, "one load moves two tokens' slices");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroup L of the launch runs on XCD L % 8 (round-robin dispatch); give
@@ -582,34 +589,32 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
   if (slot >= A.meta[0]) return;  // workgroup-uniform
   const int e = A.active[slot], p0 = A.offs[slot], p1 = A.offs[slot + 1];
   if (p0 >= p1) return;
-  const int mat = GU ? wave >> 2 : 0;  // 0: gate (or down), 1: up
-  const int tw = GU ? wave & 3 : wave;  // tile pair of the wave within the block
-  const MatArgs& M = mat ? A.m1 : A.m0;
-  const int rows = M.rows, Wr = M.words_per_row, cols = M.cols, G = cols / 64;
+  const int rows = A.m0.rows, Wr = A.m0.words_per_row, cols = A.m0.cols, G = cols / 64;
   const int NSL = (G + KSG - 1) / KSG;
   const int r = lane & 15, b = lane >> 4;
   const uint8_t* blob = expert_blob(A.blobs, A.stride, A.table, e);
+  // the wave's tiles: gate/up: the gate (u = 0) and up (u = 1) rows of one
+  // 16-row tile; down: two tiles
   int row[TPW];
   const uint32_t* cw0[TPW];
   const ST* sw0[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    row[u] = ((bx * (GU ? 4 : GMK_NW) + tw) * TPW + u) * 16 + r;
+    const MatArgs& M = (GU && (u & 1)) ? A.m1 : A.m0;
+    row[u] = GU ? ((bx * GMK_NW + wave) * (TPW / 2) + u / 2) * 16 + r
+                : ((bx * GMK_NW + wave) * TPW + u) * 16 + r;
     const int rc = min(row[u], rows - 1);
     cw0[u] = (const uint32_t*)(blob + M.codes_off) + (size_t)rc * Wr;
     sw0[u] = (const ST*)(blob + M.scales_off) + (size_t)rc * G;
   }
-  const GmkLds L = gmk_lds_layout();
+  const GmkLds L = gmk_lds_layout(TC);
   uint32_t* X = lds + L.x;
   float* Kl = (float*)(lds + L.k);
   float* osc = (float*)(lds + L.osc);
   uint32_t magic;
   asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
   const int wmap = BITS == 4 ? (b & 1) * 4 + (b >> 1) * 2 : b;
-  constexpr int UG = BITS == 4 ? 2 : 4;
-  constexpr int NU = GB / UG;
-  static_assert(GB == 8, "one scale load per lane covers a slice of eight groups");
-  // prepared vectors: pair quads [V][cols / 8] (16 bytes each), K [V][G],
+  // prepared vectors: pair quads [V][cols / 8] (16 bytes each), -K [V][G],
   // output factors [V]
   const u32x4* xq = (const u32x4*)A.prep_x;
   const float* xk = A.prep_k;
@@ -618,137 +623,149 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
   struct Batch {
     u32x4 w[TPW][NU];
     u32x4 sq[TPW];
-    float s[TPW][SV ? 1 : GB];
   };
-  auto load = [&](Batch& B, int sl) __attribute__((always_inline)) {  // slice sl (clamped) of this lane's rows
+  // weights of slice sl (clamped) for this wave: units, then scales
+  auto load_w = [&](Batch& B, int sl) __attribute__((always_inline)) {
     const int g0 = min(sl, NSL - 1) * KSG;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
+    for (int u = 0; u < TPW; ++u) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) B.w[t][u] = gm_unit_load<BITS>(cw0[t], g0 + u * UG, G, b);
+      for (int n = 0; n < NU; ++n) B.w[u][n] = gm_unit_load<BITS>(cw0[u], g0 + n * UG, G, b);
       if constexpr (SV) {
-        B.sq[t] = gm_scale_quad<ST>(sw0[t], min(g0 + 4 * (b & 1), G - 4));
+        B.sq[u] = gm_scale_quad<ST>(sw0[u], g0);  // G % 4 == 0: g0 + 4 <= G
       } else {
+        uint32_t s4[4];
 #pragma unroll
-        for (int j = 0; j < GB; ++j) B.s[t][j] = load_scale<ST, false>(sw0[t] + min(g0 + j, G - 1));
+        for (int j = 0; j < 4; ++j)
+          s4[j] = __builtin_bit_cast(uint32_t, load_scale<ST, false>(sw0[u] + min(g0 + j, G - 1)));
+        B.sq[u] = u32x4{s4[0], s4[1], s4[2], s4[3]};
       }
     }
   };
-  // SV: quarters 0 and 2 loaded quad 0 of the slice, 1 and 3 quad 1
-  auto scales = [&](const Batch& B, int t, float* sc) __attribute__((always_inline)) {
-    if constexpr (SV) {
-      uint32_t q[4] = {B.sq[t].x, B.sq[t].y, B.sq[t].z, B.sq[t].w};
+  // lane l's token of the chunk as a prepared-vector index
+  int vA = 0;
+  // token pair pp of the chunk of slice sl (clamped) into buffer buf with
+  // one direct-to-LDS load: lanes 0-31 copy the even token's 32 quads in
+  // order, lanes 32-63 the odd token's rotated by one (its quad q lands at
+  // 32 + (q + 1) % 32), so that with pair rows XPS quads apart the 16
+  // tokens an operand read touches fall on 16 different bank quads. A slice
+  // past the row's end (G not a multiple of KSG) re-reads the row's last
+  // quad, never used.
+  auto stage_x = [&](int sl, int buf, int pp) __attribute__((always_inline)) {
+    const int sc = min(sl, NSL - 1);
+    const int ve = __builtin_amdgcn_readlane(vA, 2 * pp), vo = __builtin_amdgcn_readlane(vA, 2 * pp + 1);
+    const int q = lane < 32 ? lane : (lane - 33) & 31;
+    const int qc = min(sc * QPS + q, cols / 8 - 1);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(xq + (size_t)(lane < 32 ? ve : vo) * (cols / 8) + qc),
+        (__attribute__((address_space(3))) void*)(X + buf * XB + pp * XPS * 4), 16, 0, 0);
+  };
+  // all of slice sl's loads of this wave: its weights, its token pairs and
+  // (waves 0..KSG-1) the offsets of group wave of the slice for the chunk
+  auto load_all = [&](Batch& B, int sl, int buf) __attribute__((always_inline)) {
+    load_w(B, sl);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t lo = q[i], hi = q[i];
-        swap16(lo, hi);  // lo: quad 0, hi: quad 1 (in every quarter)
-        sc[i] = __builtin_bit_cast(float, lo);
-        sc[4 + i] = __builtin_bit_cast(float, hi);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < GB; ++j) sc[j] = B.s[t][j];
+    for (int d = 0; d < PPV; ++d) stage_x(sl, buf, wave * PPV + d);
+    if (wave < KSG) {
+      const int g = min(min(sl, NSL - 1) * KSG + wave, G - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(xk + (size_t)vA * G + g),
+                                       (__attribute__((address_space(3))) void*)(Kl + buf * KB +
+                                                                                 wave * TC),
+                                       4, 0, 0);
     }
-  };
-  auto word = [&](const uint32_t (*w)[4], int j, int h) -> uint32_t {
-    if constexpr (BITS == 4) return w[j / 2][(j % 2) * 2 + h];
-    return w[j / 4][j % 4];
-  };
-  // this lane's token of the chunk (clamped) as a prepared-vector index
-  auto vec_of = [&](int pc, int nt) {
-    const int p = pc + min(lane, nt - 1);
-    return GU ? A.pair_token[p] : p;
-  };
-  // tokens of slice sl (clamped) into buffer buf: wave w copies the slices
-  // of tokens w * 8 .. w * 8 + 7, one contiguous kilobyte per load (lane i
-  // quad i), and the offsets of group w for all 64 tokens
-  auto stage = [&](int v, int sl, int buf) __attribute__((always_inline)) {
-    const int s = min(sl, NSL - 1);
-    // a slice past the row's end (G not a multiple of 8) re-reads the row's
-    // last quad; those entries are never used
-    const int qc = min(s * QPS + lane, cols / 8 - 1);
-#pragma unroll
-    for (int i = 0; i < TC / GMK_NW; ++i) {
-      const int tk = wave * (TC / GMK_NW) + i;
-      const int vt = __builtin_amdgcn_readlane(v, tk);
-      __builtin_amdgcn_global_load_lds((const void*)(xq + (size_t)vt * (cols / 8) + qc),
-                                       (__attribute__((address_space(3))) void*)(X + buf * XB +
-                                                                                 tk * GMK_XTS),
-                                       16, 0, 0);
-    }
-    const int g = min(s * KSG + wave, G - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(xk + (size_t)v * G + g),
-                                     (__attribute__((address_space(3))) void*)(Kl + buf * KB +
-                                                                               wave * TC),
-                                     4, 0, 0);
   };
 
   f32x4m acc[TPW][NTT];
-  // NA: token tiles multiplied (all four; a separate two-tile path for
-  // half-empty chunks measured slower: its registers spilled)
-  auto compute = [&](const Batch& B, int sl, int buf, auto na) __attribute__((always_inline)) {
-    constexpr int NA = decltype(na)::value;
+  // slice sl from buffer buf and batch B
+  auto compute = [&](const Batch& B, int sl, int buf) __attribute__((always_inline)) {
     const int g0 = sl * KSG;
     const int glast = min(G - 1 - g0, KSG - 1);
-    uint32_t w[TPW][NU][4];
-    float sc[TPW][GB];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      scales(B, t, sc[t]);
-#pragma unroll
-      for (int u = 0; u < NU; ++u) gm_unit_arrange<BITS>(B.w[t][u], w[t][u]);
-    }
     const uint32_t* Xb = X + buf * XB;
     const float* Kb = Kl + buf * KB;
+    uint32_t wa[TPW][4];  // the current load unit's words, arranged
 #pragma unroll
-    for (int j = 0; j < GB; ++j) {
+    for (int j = 0; j < KSG; ++j) {
       const bool own = g0 + j < G;  // wave-uniform
       const int gl = min(j, glast);
+      if (j % UG == 0) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) gm_unit_arrange<BITS>(B.w[u][j / UG], wa[u]);
+      }
       h8 op[2][TPW];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int u = 0; u < TPW; ++u)
-          op[h][u] = gm_operand<BITS>(word(w[u], j, BITS == 4 ? h : 0), BITS == 4 ? 0 : h, magic);
+          op[h][u] = BITS == 4 ? gm_operand<BITS>(wa[u][(j % 2) * 2 + h], 0, magic)
+                               : gm_operand<BITS>(wa[u][j % 4], h, magic);
+      float sj[TPW];
 #pragma unroll
-      for (int t = 0; t < NA; ++t) {
-        // the MFMAs start from -K, so they leave D - K (the offsets of the
-        // fp16 pairs and the code midpoint removed) in one chain
-        const f32x4m nk = *(const f32x4m*)(Kb + gl * TC + 16 * t + 4 * b);
-        f32x4m d[TPW];
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) d[u] = nk;
+      for (int u = 0; u < TPW; ++u) {
+        const uint32_t sv = j == 0 ? B.sq[u].x : j == 1 ? B.sq[u].y : j == 2 ? B.sq[u].z : B.sq[u].w;
+        sj[u] = own ? __builtin_bit_cast(float, sv) : 0.f;
+      }
+      // LDS operands of tile t: the two token quads and the negated offsets
+      auto rd = [&](int t, h8* av, f32x4m& nk) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int hv = BITS == 4 ? 0 : h;
           const int qd = BITS == 4 ? (gl * WPG + wmap + h) : (gl * WPG + wmap) * HALVES + hv;
-          const h8 av = __builtin_bit_cast(h8, *(const u32x4*)(Xb + (16 * t + r) * GMK_XTS + qd * 4));
+          const int pos = (r & 1) ? 32 + ((qd + 1) & 31) : qd;
+          av[h] = __builtin_bit_cast(h8, *(const u32x4*)(Xb + (8 * t + (r >> 1)) * XPS * 4 + pos * 4));
+        }
+        nk = *(const f32x4m*)(Kb + gl * TC + 16 * t + 4 * b);
+      };
+      h8 av[2][2];
+      f32x4m nk[2];
+      f32x4m d[2][TPW];
+      rd(0, av[0], nk[0]);
+#pragma unroll
+      for (int t = 0; t <= NTT; ++t) {
+        if (t + 1 < NTT) rd(t + 1, av[(t + 1) & 1], nk[(t + 1) & 1]);
+        if (t < NTT) {
+          // the MFMAs start from -K, so they leave D - K (the offsets of the
+          // fp16 pairs and the code midpoint removed) in one chain
 #pragma unroll
           for (int u = 0; u < TPW; ++u)
-            d[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, op[h][u], d[u], 0, 0, 0);
-        }
+            d[t & 1][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t & 1][0], op[0][u], nk[t & 1], 0, 0, 0);
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const float sj = own ? sc[u][j] : 0.f;
-          const float a0 = d[u].x, a1 = d[u].y, a2 = d[u].z, a3 = d[u].w;
-          acc[u][t].x = fmaf(sj, a0, acc[u][t].x);
-          acc[u][t].y = fmaf(sj, a1, acc[u][t].y);
-          acc[u][t].z = fmaf(sj, a2, acc[u][t].z);
-          acc[u][t].w = fmaf(sj, a3, acc[u][t].w);
+          for (int u = 0; u < TPW; ++u)
+            d[t & 1][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t & 1][1], op[1][u], d[t & 1][u], 0, 0, 0);
         }
+        if (t >= 1) {
+#pragma unroll
+          for (int u = 0; u < TPW; ++u) {
+            const f32x4m dv = d[(t - 1) & 1][u];
+            f32x4m& a = acc[u][t - 1];
+            a.x = fmaf(sj[u], dv.x, a.x);
+            a.y = fmaf(sj[u], dv.y, a.y);
+            a.z = fmaf(sj[u], dv.z, a.z);
+            a.w = fmaf(sj[u], dv.w, a.w);
+          }
+        }
+        // keep the pipeline as written (the scheduler would otherwise hoist
+        // every tile's LDS reads)
+        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   Batch bA, bB;
-  for (int pc = p0; pc < p1; pc += TC) {
-    const int nt = min(TC, p1 - pc);
-    if (pc > p0) __syncthreads();  // the previous chunk's LDS readers are done
-    const int v = vec_of(pc, nt);
-    load(bA, 0);
-    stage(v, 0, 0);
+  const int n = p1 - p0;
+  const int nch = (n + TC - 1) / TC, base = n / nch, extra = n % nch;
+  int pc = p0;
+  for (int c = 0; c < nch; ++c) {
+    const int nt = base + (c < extra ? 1 : 0);
+    const int na = (nt + 15) / 16;
+    if (c > 0) __syncthreads();  // the previous chunk's LDS readers are done
+    {
+      const int pa = pc + min(lane, nt - 1);
+      vA = GU ? A.pair_token[pa] : pa;
+    }
+    load_all(bA, 0, 0);
     if (wave == 0)
-      __builtin_amdgcn_global_load_lds((const void*)(xo + v),
+      __builtin_amdgcn_global_load_lds((const void*)(xo + vA),
                                        (__attribute__((address_space(3))) void*)osc, 4, 0, 0);
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
@@ -756,55 +773,41 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
       for (int t = 0; t < NTT; ++t) acc[u][t] = f32x4m{0.f, 0.f, 0.f, 0.f};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // slices in pairs; every load of the next slice is issued before the
-    // current one is multiplied, and complete before the barrier
-    auto slices = [&](auto na) __attribute__((always_inline)) {
-      for (int sl = 0; sl < NSL; sl += 2) {
-        load(bB, sl + 1);
-        stage(v, sl + 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(bA, sl, 0, na);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (sl + 1 >= NSL) break;
-        load(bA, sl + 2);
-        stage(v, sl + 2, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(bB, sl + 1, 1, na);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
-    };
-    slices(std::integral_constant<int, NTT>{});
+    // slices in pairs (constant buffer indices, so the compiler can tell the
+    // direct-to-LDS writes of one buffer from the reads of the other); every
+    // load of the next slice is issued before the current one is multiplied
+    // and complete before the barrier that ends it
+    for (int sl = 0; sl < NSL; sl += 2) {
+      if (sl + 1 < NSL) load_all(bB, sl + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(bA, sl, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (sl + 1 >= NSL) break;
+      if (sl + 2 < NSL) load_all(bA, sl + 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(bB, sl + 1, 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     // outputs: lane (r, b) holds tokens 16t + 4b .. + 3 of its rows
     if constexpr (GU) {
-      // the up waves hand their sums to the gate waves of the same tiles
-      float* xch = (float*)X;  // buffer 0 is free after the last barrier
-      if (mat == 1) {
 #pragma unroll
-        for (int u = 0; u < TPW; ++u)
+      for (int v = 0; v < TPW / 2; ++v) {
+        if (row[2 * v] >= rows) continue;
 #pragma unroll
-          for (int t = 0; t < NTT; ++t)
-            *(f32x4m*)(xch + (((tw * TPW + u) * NTT + t) * 64 + lane) * 4) = acc[u][t];
-      }
-      __syncthreads();
-      if (mat == 0) {
+        for (int t = 0; t < NTT; ++t) {
+          if (t >= na) break;
+          const float ga[4] = {acc[2 * v][t].x, acc[2 * v][t].y, acc[2 * v][t].z, acc[2 * v][t].w};
+          const float ua[4] = {acc[2 * v + 1][t].x, acc[2 * v + 1][t].y, acc[2 * v + 1][t].z,
+                               acc[2 * v + 1][t].w};
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          if (row[u] >= rows) continue;
-#pragma unroll
-          for (int t = 0; t < NTT; ++t) {
-            const f32x4m up = *(const f32x4m*)(xch + (((tw * TPW + u) * NTT + t) * 64 + lane) * 4);
-            const float ga[4] = {acc[u][t].x, acc[u][t].y, acc[u][t].z, acc[u][t].w};
-            const float ua[4] = {up.x, up.y, up.z, up.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int tk = 16 * t + 4 * b + i;
-              if (tk < nt) {
-                const float o = osc[tk];
-                const float gg = ga[i] * o, uu = ua[i] * o;
-                A.out[(size_t)(pc + tk) * rows + row[u]] = gg / (1.0f + expf(-gg)) * uu;
-              }
+          for (int i = 0; i < 4; ++i) {
+            const int tkn = 16 * t + 4 * b + i;
+            if (tkn < nt) {
+              const float o = osc[tkn];
+              const float gg = ga[i] * o, uu = ua[i] * o;
+              A.out[(size_t)(pc + tkn) * rows + row[2 * v]] = gg / (1.0f + expf(-gg)) * uu;
             }
           }
         }
@@ -815,15 +818,17 @@ __global__ __launch_bounds__(GMK_NW * 64) void k_gemm_ks(GemvArgs A) {
         if (row[u] >= rows) continue;
 #pragma unroll
         for (int t = 0; t < NTT; ++t) {
+          if (t >= na) break;
           const float va[4] = {acc[u][t].x, acc[u][t].y, acc[u][t].z, acc[u][t].w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int tk = 16 * t + 4 * b + i;
-            if (tk < nt) A.out[(size_t)(pc + tk) * rows + row[u]] = va[i] * osc[tk];
+            const int tkn = 16 * t + 4 * b + i;
+            if (tkn < nt) A.out[(size_t)(pc + tkn) * rows + row[u]] = va[i] * osc[tkn];
           }
         }
       }
     }
+    pc += nt;
   }
 }
 
@@ -851,16 +856,21 @@ static hipError_t launch_gm_nw(const GemvArgs& A, bool gate_up, int in, dim3 gri
 
 template <int BITS, typename ST>
 hipError_t launch_gm_ks(const GemvArgs& A, bool gate_up, dim3 grid, hipStream_t s) {
-  const unsigned lds = (unsigned)gmk_lds_layout().total * 4;
+  if (A.tc != GMK_TC) return hipErrorInvalidValue;
+  const unsigned lds = (unsigned)gmk_lds_layout(A.tc).total * 4;
   const dim3 block(GMK_NW * 64);
   const bool sv = A.m0.cols / 64 % 4 == 0;
   auto go = [&](auto kernel) {
     const hipError_t e = gm_allow_lds(kernel, lds);
     return e != hipSuccess ? e : launch_kernel_lds(kernel, grid, block, lds, s, A);
   };
-  if (gate_up)
-    return sv ? go(k_gemm_ks<BITS, ST, true, true>) : go(k_gemm_ks<BITS, ST, true, false>);
-  return sv ? go(k_gemm_ks<BITS, ST, false, true>) : go(k_gemm_ks<BITS, ST, false, false>);
+  auto pick = [&](auto ntt) {
+    constexpr int N = decltype(ntt)::value;
+    if (gate_up)
+      return sv ? go(k_gemm_ks<BITS, ST, true, true, N>) : go(k_gemm_ks<BITS, ST, true, false, N>);
+    return sv ? go(k_gemm_ks<BITS, ST, false, true, N>) : go(k_gemm_ks<BITS, ST, false, false, N>);
+  };
+  return pick(std::integral_constant<int, GMK_TC / 16>{});
 }
 
 template <int BITS, typename ST>

@@ -33,32 +33,31 @@ __host__ __device__ inline GmLds gm_lds_layout(int cols, int tc, bool split, int
 }
 
 // K-sliced matrix-core stage (k_gemm_ks): shape and LDS layout.
-constexpr int GMK_NW = 8;   // waves per workgroup, one 16-row tile each
+constexpr int GMK_NW = 8;   // waves per workgroup
+constexpr int GMK_TPW = 2;  // 16-row tiles per wave
+constexpr int GMK_KSG = 4;  // scale groups per K slice (256 weights)
+constexpr int GMK_QPS = GMK_KSG * 8;  // 16-byte pair quads of one token's slice
 constexpr int GMK_TC = 64;  // tokens per chunk: four MFMA token tiles
-constexpr int GMK_KSG = 8;  // scale groups per K slice
-// 16-row tiles per wave: two when every row holds whole quads of scale
-// groups (vector scale loads), else one
-__host__ __device__ constexpr int gmk_tpw(bool sv) { return sv ? 2 : 1; }
-// rows of one matrix per workgroup: gate/up 4 waves per matrix, down 8
-__host__ __device__ constexpr int gmk_rows_per_block(bool gate_up, bool sv) {
-  return (gate_up ? 4 : GMK_NW) * gmk_tpw(sv) * 16;
+// rows of one matrix per workgroup: gate/up one tile of gate and up rows per
+// wave, down two tiles per wave
+__host__ __device__ constexpr int gmk_rows_per_block(bool gate_up) {
+  return (gate_up ? GMK_TPW / 2 : GMK_TPW) * GMK_NW * 16;
 }
 
-// a token's slice in LDS: KSG * 8 pair quads and one quad of padding, so
-// that the rows of 16 consecutive tokens start on 16 different bank quads
-constexpr int GMK_XTS = (GMK_KSG * 8 + 1) * 4;  // 32-bit words per token row
+// two tokens' slices in LDS (one direct-to-LDS load): 2 * GMK_QPS quads and
+// two of padding, so that pair rows start two bank quads apart
+constexpr int GMK_XPS = 2 * GMK_QPS + 2;  // 16-byte quads per token pair row
 
 struct GmkLds {
-  int x, k, s, osc, total;  // offsets and size in 32-bit words
+  int x, k, osc, total;  // offsets and size in 32-bit words
 };
 
-__host__ __device__ inline GmkLds gmk_lds_layout() {
+__host__ __device__ inline GmkLds gmk_lds_layout(int tc) {
   GmkLds L;
-  L.x = 0;                                     // 2 buffers of TC token rows
-  L.k = L.x + 2 * GMK_TC * GMK_XTS;            // 2 buffers of KSG * TC offsets
-  L.s = L.k + 2 * GMK_KSG * GMK_TC;            // per-token power-of-two scale
-  L.osc = L.s + GMK_TC;                        // per-token output factor
-  L.total = L.osc + GMK_TC;
+  L.x = 0;                               // 2 buffers of tc / 2 token pair rows
+  L.k = L.x + tc * GMK_XPS * 4;          // 2 buffers of KSG * tc negated offsets
+  L.osc = L.k + 2 * GMK_KSG * tc;        // per-token output factor
+  L.total = L.osc + tc;
   return L;
 }
 
@@ -107,9 +106,9 @@ struct GemvArgs {
 template <int BITS, typename ST>
 hipError_t launch_gm(const GemvArgs& A, bool gate_up, int in, int nw, dim3 grid, unsigned lds,
                      hipStream_t s);
-// K-sliced matrix-core stage for slots of many tokens (64 per chunk, 8 waves,
-// one 16-row tile per wave); routed experts, bf16 tokens (gate/up) or fp32 h
-// (down). Grid (ceil(rows / 128), slots).
+// K-sliced matrix-core stage for slots of many tokens (A.tc = 64 per chunk,
+// 8 waves); routed experts, bf16 tokens (gate/up) or fp32 h (down).
+// Grid (ceil(rows / gmk_rows_per_block(gate_up)), slots).
 template <int BITS, typename ST>
 hipError_t launch_gm_ks(const GemvArgs& A, bool gate_up, dim3 grid, hipStream_t s);
 

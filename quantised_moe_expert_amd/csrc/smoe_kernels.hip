@@ -659,8 +659,9 @@ static hipError_t gmk_dispatch(const LayerInfo& L, GemvArgs& A, bool gate_up, co
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int rpb = gmk_rows_per_block(gate_up, cols / 64 % 4 == 0);
+  const int rpb = gmk_rows_per_block(gate_up);
   const dim3 grid((rows + rpb - 1) / rpb, slots);
+  A.tc = GMK_TC;
   if (L.desc.bits == 4)
     return L.desc.scale_dtype == SMOE_SCALE_F32 ? launch_gm_ks<4, float>(A, gate_up, grid, s)
                                                 : launch_gm_ks<4, _Float16>(A, gate_up, grid, s);
