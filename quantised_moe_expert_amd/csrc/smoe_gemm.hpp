@@ -40,7 +40,13 @@ constexpr int GM_GB = 8;
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f32x4m __attribute__((ext_vector_type(4)));
 
-// Stage pairs [pc, pc + nt) of the slot for the matrix-core stage.
+// Stage pairs [pc, pc + nt) of the slot for the matrix-core stage. Two
+// passes over the activations: the largest magnitude and sum of squares of
+// every token, then the fp16 pairs of every (token, code word) with the
+// group offsets K summed across the WPG lanes that hold a group. In both,
+// each thread has NB loads in flight before it uses any (under a weight
+// stream a load takes microseconds, so staging costs a few round trips,
+// not one or more per token).
 template <int BITS, int IN, bool GU, int NW>
 __device__ __forceinline__ void gm_stage(const GemvArgs& A, const MatArgs& M, uint32_t* lds,
                                          const GmLds& L, int pc, int nt) {
@@ -48,32 +54,49 @@ __device__ __forceinline__ void gm_stage(const GemvArgs& A, const MatArgs& M, ui
   constexpr int WPG = QT<BITS>::WPG;  // words per group
   constexpr bool XF32 = IN != GV_BF16, SPLIT = IN == GV_F32_SPLIT;
   constexpr int NT = NW * 64;
+  constexpr int VW = XF32 ? WPW : WPW / 2;  // registers of one loaded word
+  constexpr int NB = VW >= 16 ? 1 : 16 / VW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cols = M.cols, Wr = M.words_per_row, G = cols / 64, TC = A.tc;
+  const int cols = M.cols, Wr = M.words_per_row, TC = A.tc;
   const size_t esz = XF32 ? 4 : 2;
+  // lane l (< nt) holds the activation row of the chunk's token l
+  const int tl = pc + min(lane, nt - 1);
+  const int rowl = (GU && !A.shared) ? A.pair_token[tl] : tl;
   auto vec = [&](int i) {
-    const int p = pc + i;
-    const int t = (GU && !A.shared) ? A.pair_token[p] : p;
+    const int t = __builtin_amdgcn_readlane(rowl, i);
     return (const void*)((const uint8_t*)A.x + (size_t)t * A.x_ld * esz);
   };
   float* red = (float*)(lds + L.red);
-  for (int i = 0; i < nt; ++i) {
-    const void* v = vec(i);
-    float amax = 0.f, ss = 0.f;
-    for (int cw = tid; cw < Wr; cw += NT) {
-      float xv[WPW];
-      gv_load_word<BITS, XF32>(v, cw, xv);
+  for (int i0 = 0; i0 < nt; i0 += NB) {
+    float amax[NB], ss[NB];
 #pragma unroll
-      for (int j = 0; j < WPW; ++j) {
-        amax = fmaxf(amax, fabsf(xv[j]));
-        ss = fmaf(xv[j], xv[j], ss);
+    for (int q = 0; q < NB; ++q) amax[q] = ss[q] = 0.f;
+    for (int cw = tid; cw < Wr; cw += NT) {
+      float xv[NB][WPW];
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        if (i0 + q < nt) {  // uniform
+          gv_load_word<BITS, XF32>(vec(i0 + q), cw, xv[q]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < WPW; ++j) xv[q][j] = 0.f;
+        }
       }
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int j = 0; j < WPW; ++j) {
+          amax[q] = fmaxf(amax[q], fabsf(xv[q][j]));
+          ss[q] = fmaf(xv[q][j], xv[q][j], ss[q]);
+        }
     }
-    amax = lane63(seg_max(amax, 6));
-    ss = lane63(seg_sum(ss, 6));
-    if (lane == 0) {
-      red[(i * NW + wave) * 2] = amax;
-      red[(i * NW + wave) * 2 + 1] = ss;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const float m = lane63(seg_max(amax[q], 6)), s2 = lane63(seg_sum(ss[q], 6));
+      if (lane == 0 && i0 + q < nt) {
+        red[((i0 + q) * NW + wave) * 2] = m;
+        red[((i0 + q) * NW + wave) * 2 + 1] = s2;
+      }
     }
   }
   __syncthreads();
@@ -81,55 +104,77 @@ __device__ __forceinline__ void gm_stage(const GemvArgs& A, const MatArgs& M, ui
   float* osc = (float*)(lds + L.osc);
   uint32_t* X = lds + L.x;
   uint32_t* Xlo = lds + L.xlo;
-  // unit (g, i): group g of token i; pairs of word cw for token i go to
-  // X[((cw * HALVES + hv) * TC + i) * 4 + (q % 4)] with hv = q / 4 (split
-  // inputs: the hi halves there, the lo halves at the same place in Xlo)
-  constexpr int HALVES = PPW / 4;
-  for (int u = tid; u < G * nt; u += NT) {
-    const int i = u / G, g = u - i * G;
+  // per token: the power-of-two scale S (kept where its first partial was)
+  // and the output factor
+  if (tid < nt) {
     float m = 0.f, q2 = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      m = fmaxf(m, red[(i * NW + w) * 2]);
-      q2 += red[(i * NW + w) * 2 + 1];
+      m = fmaxf(m, red[(tid * NW + w) * 2]);
+      q2 += red[(tid * NW + w) * 2 + 1];
     }
     int ex = 0;
     frexpf(m, &ex);
     ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
     const float S = ldexpf(1.0f, 14 - ex);
-    if (g == 0) {
-      const float r = A.rms ? 1.0f / sqrtf(q2 / (float)cols + A.eps) : 1.0f;
-      osc[i] = r / (QT<BITS>::M * S);
-    }
-    const void* v = vec(i);
-    float kk = 0.f;
-#pragma unroll 2
-    for (int j = 0; j < WPG; ++j) {
-      const int cw = g * WPG + j;
-      float xv[WPW];
-      gv_load_word<BITS, XF32>(v, cw, xv);
+    const float r = A.rms ? 1.0f / sqrtf(q2 / (float)cols + A.eps) : 1.0f;
+    osc[tid] = r / (QT<BITS>::M * S);
+    red[tid * NW * 2] = S;
+  }
+  __syncthreads();
+  // unit u: code word cw = u % Wr of token i = u / Wr; its pairs go to
+  // X[((cw * HALVES + hv) * TC + i) * 4 + (q % 4)] with hv = q / 4 (split
+  // inputs: the hi halves there, the lo halves at the same place in Xlo).
+  // Wr and NT are multiples of WPG, so the WPG lanes of a group's words are
+  // consecutive and belong to one token.
+  constexpr int HALVES = PPW / 4;
+  constexpr int LGW = WPG == 8 ? 3 : 2;
+  static_assert((1 << LGW) == WPG, "words per group");
+  const int nu = nt * Wr;
+  for (int u0 = 0; u0 < nu; u0 += NT * NB) {
+    float xv[NB][WPW];
 #pragma unroll
-      for (int q = 0; q < PPW; ++q) {
-        const int hs = q / NPOS, pos = q % NPOS;
+    for (int q = 0; q < NB; ++q) {
+      const int u = u0 + q * NT + tid;
+      const int i = min(u / Wr, nt - 1);
+      const int ti = __shfl(rowl, i, 64);  // every lane takes part
+      if (u < nu) {
+        gv_load_word<BITS, XF32>((const uint8_t*)A.x + (size_t)ti * A.x_ld * esz, u - i * Wr, xv[q]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < WPW; ++j) xv[q][j] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int u = u0 + q * NT + tid;
+      const bool in = u < nu;
+      const int i = in ? u / Wr : 0, cw = in ? u - i * Wr : 0;
+      const float S = red[i * NW * 2];
+      float kk = 0.f;
+#pragma unroll
+      for (int qq = 0; qq < PPW; ++qq) {
+        const int hs = qq / NPOS, pos = qq % NPOS;
         const int ia = hs * NPOS + pos, ib = ia + WPW / 2;
         const float f = S * (1.0f / (float)(1 << (BITS * pos)));
-        const float a = xv[ia] * f, bb = xv[ib] * f;
+        const float a = xv[q][ia] * f, bb = xv[q][ib] * f;
         const _Float16 ha = (_Float16)a, hb = (_Float16)bb;
-        const int xi = ((cw * HALVES + q / 4) * TC + i) * 4 + (q % 4);
-        X[xi] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
+        const int xi = ((cw * HALVES + qq / 4) * TC + i) * 4 + (qq % 4);
+        if (in) X[xi] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
         float sumx = (float)ha + (float)hb;
         if constexpr (SPLIT) {
           const _Float16 la = (_Float16)(a - (float)ha), lb = (_Float16)(bb - (float)hb);
-          Xlo[xi] = __builtin_bit_cast(uint32_t, f16x2{la, lb});
+          if (in) Xlo[xi] = __builtin_bit_cast(uint32_t, f16x2{la, lb});
           sumx += (float)la + (float)lb;
         }
         kk = fmaf(sumx, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)), kk);
       }
+      kk = seg_sum(kk, LGW);
+      if (in && (cw & (WPG - 1)) == WPG - 1) Kl[(cw / WPG) * 16 + i] = kk;
     }
-    Kl[g * 16 + i] = kk;
   }
   // K of the token rows past the chunk (their D rows are never used)
-  for (int u = tid; u < G * 16; u += NT)
+  for (int u = tid; u < (cols / 64) * 16; u += NT)
     if ((u & 15) >= nt) Kl[u] = 0.f;
   __syncthreads();
 }
@@ -248,8 +293,13 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
     p1 = A.T;
     blob = A.blobs;
   } else {
-    const int slot = blockIdx.y, nr = A.meta[0];
-    if (slot >= nr + A.nsh) return;  // workgroup-uniform
+    // the shared expert's parts take the first rows of the grid: their
+    // workgroups (every token of the batch each) are then dispatched ahead
+    // of the routed slots' instead of starting last, when a grid larger than
+    // the GPU holds at once leaves them to a second round
+    const int y = blockIdx.y, nr = A.meta[0], nsh = A.nsh;
+    const int slot = y < nsh ? nr + y : y - nsh;
+    if (y >= nsh && slot >= nr) return;  // workgroup-uniform
     p0 = A.offs[slot];
     p1 = A.offs[slot + 1];
     if (slot < nr) {
