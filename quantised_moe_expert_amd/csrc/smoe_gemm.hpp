@@ -170,7 +170,8 @@ __device__ __forceinline__ void gm_stage(const GemvArgs& A, const MatArgs& M, ui
         kk = fmaf(sumx, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)), kk);
       }
       kk = seg_sum(kk, LGW);
-      if (in && (cw & (WPG - 1)) == WPG - 1) Kl[(cw / WPG) * 16 + i] = kk;
+      // stored negated: the MFMA chains start from it
+      if (in && (cw & (WPG - 1)) == WPG - 1) Kl[(cw / WPG) * 16 + i] = -kk;
     }
   }
   // K of the token rows past the chunk (their D rows are never used)
@@ -469,7 +470,10 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
         const bool own = g0 + j < gb1;  // wave-uniform
         const int g = min(g0 + j, G - 1);
         const float sa = own ? bsa[j] : 0.f;
-        f32x4m da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
+        // both chains start from -K, so they leave D - K (the offsets of the
+        // fp16 pairs and the code midpoint removed)
+        const f32x4m nk = *(const f32x4m*)(Kl + g * 16 + 4 * b);
+        f32x4m da = nk, db = nk;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int hv = BITS == 4 ? 0 : h;
@@ -489,20 +493,16 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
             if constexpr (GU) db = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, ob, db, 0, 0, 0);
           }
         }
-        const f32x4m kv = *(const f32x4m*)(Kl + g * 16 + 4 * b);
-        const float a0 = da.x, a1 = da.y, a2 = da.z, a3 = da.w;
-        const float k0 = kv.x, k1 = kv.y, k2 = kv.z, k3 = kv.w;
-        acc_a.x = fmaf(sa, a0 - k0, acc_a.x);
-        acc_a.y = fmaf(sa, a1 - k1, acc_a.y);
-        acc_a.z = fmaf(sa, a2 - k2, acc_a.z);
-        acc_a.w = fmaf(sa, a3 - k3, acc_a.w);
+        acc_a.x = fmaf(sa, da.x, acc_a.x);
+        acc_a.y = fmaf(sa, da.y, acc_a.y);
+        acc_a.z = fmaf(sa, da.z, acc_a.z);
+        acc_a.w = fmaf(sa, da.w, acc_a.w);
         if constexpr (GU) {
           const float sb = own ? bsb[j] : 0.f;
-          const float b0 = db.x, b1 = db.y, b2 = db.z, b3 = db.w;
-          acc_b.x = fmaf(sb, b0 - k0, acc_b.x);
-          acc_b.y = fmaf(sb, b1 - k1, acc_b.y);
-          acc_b.z = fmaf(sb, b2 - k2, acc_b.z);
-          acc_b.w = fmaf(sb, b3 - k3, acc_b.w);
+          acc_b.x = fmaf(sb, db.x, acc_b.x);
+          acc_b.y = fmaf(sb, db.y, acc_b.y);
+          acc_b.z = fmaf(sb, db.z, acc_b.z);
+          acc_b.w = fmaf(sb, db.w, acc_b.w);
         }
       }
     };
