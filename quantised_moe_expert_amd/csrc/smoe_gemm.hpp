@@ -436,14 +436,14 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
   };
 
   Batch bA, bB;
-  load(bA, 0);  // in flight while the tokens are staged
   for (int pc = p0; pc < p1; pc += TC) {
     const int nt = min(TC, p1 - pc);
-    if (pc > p0) {
-      __syncthreads();  // the previous chunk's readers are done
-      load(bA, 0);
-    }
+    if (pc > p0) __syncthreads();  // the previous chunk's readers are done
+    // the tokens are staged before the first weight batch is requested:
+    // loads retire in order, so staging loads issued behind a weight batch
+    // would wait for it
     gm_stage<BITS, IN, GU, NW>(A, M0, lds, L, pc, nt);
+    load(bA, 0);
     // A row r of the MFMAs is token r; rows past the chunk read whatever the
     // LDS holds (row TC - 1 past the staged block) and their D rows are
     // never used
