@@ -448,6 +448,17 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
     // LDS holds (row TC - 1 past the staged block) and their D rows are
     // never used
     const int rr = min(r, TC - 1);
+    // LDS word offset of this lane's A operand for MFMA h of group g: word
+    // cw of a group sits at ((cw * HALVES + hv) * TC + rr) * 4, which is
+    // g * gstride (uniform) plus a per-lane part fixed for the chunk
+    const int gstride = WPG * HALVES * TC * 4;
+    int xoff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int hv = BITS == 4 ? 0 : h;
+      const int cwl = BITS == 4 ? wmap + h : wmap;
+      xoff[h] = ((cwl * HALVES + hv) * TC + rr) * 4;
+    }
     f32x4m acc_a = {0.f, 0.f, 0.f, 0.f}, acc_b = {0.f, 0.f, 0.f, 0.f};
     // batch k; groups at or past gb1 (the tail of the wave's range) count
     // with scale zero and read the last group's LDS
@@ -477,8 +488,7 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int hv = BITS == 4 ? 0 : h;
-          const int cw = BITS == 4 ? g * WPG + wmap + h : g * WPG + wmap;
-          const int xi = ((cw * HALVES + hv) * TC + rr) * 4;
+          const int xi = g * gstride + xoff[h];
           const h8 av = __builtin_bit_cast(h8, *(const u32x4*)(X + xi));
           const h8 oa = gm_operand<BITS>(word(wa, j, BITS == 4 ? h : 0), hv, magic);
           da = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, oa, da, 0, 0, 0);
