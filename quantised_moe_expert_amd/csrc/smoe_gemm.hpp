@@ -591,11 +591,10 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
 //
 // For slots with many tokens (prefill-sized batches) each weight fetch
 // should serve more tokens than one MFMA's 16, but a 4096-wide token vector
-// takes 8 KB of LDS as fp16, so a chunk of 64 or 128 tokens does not fit
-// whole. This stage takes the chunk one K slice (four scale groups, 256
-// weights) at a time into one of two LDS buffers and feeds every decoded
-// weight operand to NTT MFMA token tiles, so a slot's weights are read once
-// per chunk.
+// takes 8 KB of LDS as fp16, so a chunk of 64 tokens does not fit whole.
+// This stage takes the chunk one K slice (four scale groups, 256 weights) at
+// a time into one of two LDS buffers and feeds every decoded weight operand
+// to NTT = 4 MFMA token tiles, so a slot's weights are read once per chunk.
 //   - The token vectors were converted beforehand (k_gmk_prep) into the
 //     fp16 pairs, group offsets K and output factors of k_gemm's staging,
 //     stored per vector in the order of the MFMA operand, so a slice is
@@ -603,10 +602,9 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
 //     lane i writes 16 bytes at LDS base + 16 i), no registers and no
 //     conversion in this kernel. Such a load costs the CU about 48 cycles of
 //     issue whatever its size, so each one moves a whole kilobyte (two
-//     tokens' 512-byte slices) and they are spread one per scale group over
-//     the slice being multiplied. In LDS a pair's row is 66 quads long and
-//     the odd token's quads are rotated by one, so the 16 tokens an MFMA
-//     operand read touches sit on 16 different bank quads.
+//     tokens' 512-byte slices). In LDS a pair's row is 66 quads long and the
+//     odd token's quads are rotated by one, so the 16 tokens an MFMA operand
+//     read touches sit on 16 different bank quads.
 //   - Each wave owns two 16-row tiles: for gate/up the gate and the up rows
 //     of the same 16 rows (SwiGLU is then applied in registers), for down
 //     two adjacent tiles. Each token operand read from LDS feeds both tiles.
@@ -614,7 +612,8 @@ __global__ __launch_bounds__(NW * 64, (BITS == 2 && !GU && NW == 4) ? 4 : 1) voi
 //     LDS buffer) are requested before the current slice is multiplied; one
 //     wait for the wave's loads and one barrier end the slice.
 //   - A slot's tokens are cut into chunks of nearly equal size; token rows
-//     past the chunk's end read stale LDS rows, whose sums are dropped.
+//     past the chunk's end repeat its last token, and their sums are
+//     dropped.
 //   - Within a group the LDS operands of tile t + 1 are read while tile t is
 //     multiplied, and tile t - 1's sums are scaled after tile t's MFMAs are
 //     issued, so no vector instruction waits on an MFMA it just issued.
