@@ -232,9 +232,10 @@ int smoe_route_ex(const float* d_logits, int n_tokens, int n_experts, int top_k,
  *             256-byte aligned; contents are scratch and need no clearing.
  * Tokens that share an expert read its weights once per call.
  * Errors: SMOE_E_ARG, SMOE_E_WORKSPACE, SMOE_E_UNSUPPORTED (the grouping's
- * per-expert token bitmasks and counts, (num_experts * (w + ceil(w / 8) + 3)
- * + 1) * 4 bytes with w = ceil(n_tokens / 32), exceed 160 KB: e.g. more than
- * ~2150 tokens with 512 experts), SMOE_E_HIP. n_tokens == 0 is a no-op.
+ * per-expert token bitmasks and counts, (num_experts * ((w | 1) +
+ * (ceil(w / 8) | 1) + 3) + 1) * 4 bytes with w = ceil(n_tokens / 32), exceed
+ * 160 KB: e.g. more than 2144 tokens with 512 experts), SMOE_E_HIP.
+ * n_tokens == 0 is a no-op.
  * Activations must be finite with |x| < 2^100 (they are rescaled by a power
  * of two per vector before the fp16 dot products). */
 int smoe_moe_forward(const smoe_layer* layer, const void* d_x, int x_dtype,

@@ -78,12 +78,13 @@ enum XMode : int {
   X_F32_RMS = 2,    // fp32 residual stream; the stage applies unit-gain RMSNorm
 };
 
-// Grouping (T > 1) keeps in LDS a token bitmask per expert (E * ceil(T / 32)
-// words), the token counts before every eighth word of it (E * ceil(T / 256)
-// words) and 3 E + 1 words of slot bookkeeping; at most 160 KB.
+// Grouping (T > 1) keeps in LDS a token bitmask per expert (ceil(T / 32)
+// words), the token counts before every eighth word of it (ceil(T / 256)
+// words), both rows padded to an odd number of words, and 3 E + 1 words of
+// slot bookkeeping; at most 160 KB.
 inline int64_t group_lds_bytes(int E, int T) {
   const int64_t tw = (T + 31) / 32, tw8 = (tw + 7) / 8;
-  return ((int64_t)E * (tw + tw8 + 3) + 1) * 4;
+  return ((int64_t)E * ((tw | 1) + (tw8 | 1) + 3) + 1) * 4;
 }
 inline bool group_fits(int E, int T) { return group_lds_bytes(E, T) <= 160 * 1024; }
 

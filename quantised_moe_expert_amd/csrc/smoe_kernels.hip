@@ -277,40 +277,70 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk(RouteArgs A) {
 
 // Grouping of the T*k (token, slot) pairs by expert, one workgroup: active
 // experts ascending, and inside an expert the pairs in ascending token order,
-// so the grouping is unique.
+// so the grouping is unique. The selected ids are read GROUP_BATCH per thread
+// at a time, all loads of a batch issued before the first is used; the first
+// batch's ids stay in registers for the last pass. The lanes of a wave hold
+// pairs of a few neighbouring tokens and many experts, so they touch the same
+// word of different experts' rows: the rows are an odd number of words long,
+// which puts those words in different LDS banks (with an even length they
+// share one bank, and every such access is serialised lane by lane).
 constexpr int GROUP_THREADS = 1024;
+constexpr int GROUP_BATCH = 16;
 
 __global__ __launch_bounds__(GROUP_THREADS) void k_group(RouteArgs A) {
   extern __shared__ uint32_t lds[];
   const int TW = (A.T + 31) >> 5, TW8 = (TW + 7) >> 3;
-  uint32_t* sel = lds;                          // [E][TW] token bitmask per expert
-  int* pre8 = (int*)(sel + A.E * TW);           // [E][TW8] tokens before every 8th word
-  int* slot_of = pre8 + A.E * TW8;              // [E]
+  const int TWS = TW | 1, TW8S = TW8 | 1;        // row strides (odd)
+  uint32_t* sel = lds;                          // [E][TWS] token bitmask per expert
+  int* pre8 = (int*)(sel + A.E * TWS);          // [E][TW8S] tokens before every 8th word
+  int* slot_of = pre8 + A.E * TW8S;             // [E]
   int* cnt = slot_of + A.E;                     // [E]
   int* offs = cnt + A.E;                        // [E + 1] (slot order)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = A.T * A.k;
-  for (int i = tid; i < A.E * TW; i += blockDim.x) sel[i] = 0u;
+  constexpr int CH = GROUP_THREADS * GROUP_BATCH;  // pairs per batch
+  // expert ids of pairs c + u * GROUP_THREADS + tid (-1 past the end)
+  auto load_ids = [&](int c, int (&id)[GROUP_BATCH]) {
+#pragma unroll
+    for (int u = 0; u < GROUP_BATCH; ++u) {
+      const int i = c + u * GROUP_THREADS + tid;
+      id[u] = i < P ? A.ids[i] : -1;
+    }
+  };
+  auto mark = [&](int c, const int (&id)[GROUP_BATCH]) {
+#pragma unroll
+    for (int u = 0; u < GROUP_BATCH; ++u) {
+      if (id[u] >= 0) {
+        const int t = (c + u * GROUP_THREADS + tid) / A.k;
+        atomicOr(&sel[id[u] * TWS + (t >> 5)], 1u << (t & 31));
+      }
+    }
+  };
+  int id0[GROUP_BATCH];
+  load_ids(0, id0);
+  for (int i = tid; i < A.E * TWS; i += GROUP_THREADS) sel[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < P; i += blockDim.x) {
-    const int t = i / A.k;
-    atomicOr(&sel[A.ids[i] * TW + (t >> 5)], 1u << (t & 31));
+  mark(0, id0);
+  for (int c = CH; c < P; c += CH) {
+    int id[GROUP_BATCH];
+    load_ids(c, id);
+    mark(c, id);
   }
   __syncthreads();
   // per expert and block of eight words: tokens before the block (threads
   // take (expert, block) pairs; each expert's blocks are then summed up)
-  for (int u = tid; u < A.E * TW8; u += blockDim.x) {
+  for (int u = tid; u < A.E * TW8; u += GROUP_THREADS) {
     const int e = u / TW8, q8 = u - e * TW8;
     int c = 0;
-    for (int q = q8 * 8; q < min(q8 * 8 + 8, TW); ++q) c += __popc(sel[e * TW + q]);
-    pre8[u] = c;
+    for (int q = q8 * 8; q < min(q8 * 8 + 8, TW); ++q) c += __popc(sel[e * TWS + q]);
+    pre8[e * TW8S + q8] = c;
   }
   __syncthreads();
-  for (int e = tid; e < A.E; e += blockDim.x) {
+  for (int e = tid; e < A.E; e += GROUP_THREADS) {
     int c = 0;
     for (int q8 = 0; q8 < TW8; ++q8) {
-      const int b = pre8[e * TW8 + q8];
-      pre8[e * TW8 + q8] = c;
+      const int b = pre8[e * TW8S + q8];
+      pre8[e * TW8S + q8] = c;
       c += b;
     }
     cnt[e] = c;
@@ -348,22 +378,34 @@ __global__ __launch_bounds__(GROUP_THREADS) void k_group(RouteArgs A) {
     }
   }
   // the shared-expert slots: pair P + v * T + t is token t
-  for (int i = tid; i < A.nsh * A.T; i += blockDim.x) A.pair_token[P + i] = i % A.T;
+  for (int i = tid; i < A.nsh * A.T; i += GROUP_THREADS) A.pair_token[P + i] = i % A.T;
   __syncthreads();
   // pair (t, j): its rank among the expert's tokens is the tokens before its
   // word's block, plus the words of the block before its word, plus the bits
   // below it in its word
-  for (int i = tid; i < P; i += blockDim.x) {
-    const int t = i / A.k;
-    const int e = A.ids[i];
-    const uint32_t* row = sel + e * TW;
-    const int q = t >> 5;
-    int rank = pre8[e * TW8 + (q >> 3)];
-    for (int qq = q & ~7; qq < q; ++qq) rank += __popc(row[qq]);
-    rank += __popc(row[q] & ((1u << (t & 31)) - 1u));
-    const int pos = offs[slot_of[e]] + rank;
-    A.pair_token[pos] = t;
-    A.pair_of[i] = pos;
+  auto place = [&](int c, const int (&id)[GROUP_BATCH]) {
+#pragma unroll
+    for (int u = 0; u < GROUP_BATCH; ++u) {
+      const int e = id[u];
+      if (e >= 0) {
+        const int i = c + u * GROUP_THREADS + tid;
+        const int t = i / A.k;
+        const uint32_t* row = sel + e * TWS;
+        const int q = t >> 5;
+        int rank = pre8[e * TW8S + (q >> 3)];
+        for (int qq = q & ~7; qq < q; ++qq) rank += __popc(row[qq]);
+        rank += __popc(row[q] & ((1u << (t & 31)) - 1u));
+        const int pos = offs[slot_of[e]] + rank;
+        A.pair_token[pos] = t;
+        A.pair_of[i] = pos;
+      }
+    }
+  };
+  place(0, id0);
+  for (int c = CH; c < P; c += CH) {
+    int id[GROUP_BATCH];
+    load_ids(c, id);
+    place(c, id);
   }
 }
 

@@ -88,6 +88,10 @@ def test_grouping_that_does_not_fit_lds_is_unsupported():
     try:
         assert smoe.smoe_workspace_bytes(h, 4096, 8) == 0
         assert smoe.smoe_workspace_bytes(h, 2048, 8) > 0
+        # the edge: 2144 tokens take 67 + 9 + 3 words per expert (161,796 B),
+        # 2145 tokens 69 + 9 + 3 (the bitmask rows padded to odd lengths)
+        assert smoe.smoe_workspace_bytes(h, 2144, 8) > 0
+        assert smoe.smoe_workspace_bytes(h, 2145, 8) == 0
         with pytest.raises(smoe.SmoeError) as e:
             smoe.smoe_moe_forward(h, FAKE, smoe.SMOE_DTYPE_BF16, FAKE, 4096, 8, True, FAKE, 0, 0,
                                   FAKE, 1 << 40, 0)

@@ -399,7 +399,9 @@ def test_qwen235b_q4_t512_sampled():
 
 
 def test_max_tokens_grouping_beyond_64k_lds():
-    # 4096 tokens over 128 experts: the grouping's token bitmasks take 65.5 KB
+    # 4096 tokens over 128 experts: the grouping's token bitmasks take 65.5 KB,
+    # and its 32768 pairs take two batches of id loads; every token is checked
+    # (a pair placed in another's position changes two tokens' outputs)
     _torch()
     import quantised_moe_expert_amd as smoe
     T = smoe.SMOE_MAX_TOKENS
@@ -407,7 +409,15 @@ def test_max_tokens_grouping_beyond_64k_lds():
     r = synth.rng(78)
     x = _x(r, T, 256, "bf16")
     lg = synth.normal_f32(r, (T, 128))
-    _check_layer(hl, x, lg, 8, True, "bf16", tokens=[0, 1, 2047, T - 1])
+    print(f"grouping: all {T} tokens, d 256, ffn 128, 128 experts, top-8", flush=True)
+    out, ids, w = DeviceLayer(hl).forward(x, lg, 8, True, "bf16")
+    ref, routes = oracle_by_expert(hl.oracle(), x, lg, 8, True)
+    for t, (want, wt) in enumerate(routes):
+        assert ids[t].tolist() == want, (t, ids[t], want)
+        assert np.allclose(w[t], wt, rtol=1e-5, atol=1e-7)
+    assert np.all(np.isfinite(out))
+    per_tok = [rel_l2(out[t], ref[t]) for t in range(T)]
+    assert rel_l2(out, ref) <= TOL and max(per_tok) <= TOL, (rel_l2(out, ref), max(per_tok))
 
 
 def test_deepseek16b_q4_b8_full():
