@@ -132,6 +132,17 @@ def test_small_layers(case, x_dtype):
     _check_layer(hl, x, lg, k, norm, x_dtype)
 
 
+# Routing and grouping of batches around 64 tokens, up to 16 selections per
+# token, 512 experts, every expert selected, and one selection per token.
+@pytest.mark.parametrize("T,E,k", [(64, 256, 16), (65, 256, 16), (64, 512, 8), (2, 3, 3),
+                                   (33, 64, 1)])
+def test_route_group_batch_edges(T, E, k):
+    _torch()
+    hl = random_layer(90 + T + E, 256, 128, E, 4, "f16")
+    r = synth.rng(91 + T)
+    _check_layer(hl, _x(r, T, 256, "bf16"), synth.normal_f32(r, (T, E)), k, True, "bf16")
+
+
 # the widest activation vectors the library registers (wider ones are
 # refused at load): one token, and batches through the grouped stages
 @pytest.mark.parametrize("d,ffn,shared", [(11392, 128, 0), (128, 19072, 19072)])
