@@ -67,9 +67,12 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
   const int bits = (int)L.desc.bits;
   GuLaunch gu;
   DnLaunch dn;
-  if (!find_pair(bits, (int)L.desc.scale_dtype, P.gate.v, P.down.v, xf32, &gu, &dn))
+  // the down rows go to at most 16 lanes each (see k_dec_down)
+  const int lg_d = P.down.lpr_log2 < 4 ? P.down.lpr_log2 : 4;
+  const int vd = P.down.words_per_row >> lg_d;
+  if (!find_pair(bits, (int)L.desc.scale_dtype, P.gate.v, vd, xf32, &gu, &dn))
     return hipSuccess;
-  const int rpwd = 64 >> P.down.lpr_log2;
+  const int rpwd = 64 >> lg_d;
   int rb = (P.d_model + DEC_NWG - 1) / DEC_NWG;
   rb = (rb + rpwd - 1) / rpwd * rpwd;
   // shape limits of the kernels' register and LDS staging
@@ -94,7 +97,7 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
   A.k = k;
   A.norm = norm;
   A.lg_g = P.gate.lpr_log2;
-  A.lg_d = P.down.lpr_log2;
+  A.lg_d = lg_d;
   A.x = x;
   A.rms = rms ? 1 : 0;
   A.eps = eps;

@@ -20,11 +20,14 @@
 //     computes any, then stores h[j, r] = silu(gate_r . x) * (up_r . x).
 // K2 (k_dec_down), NWG workgroups x 8 waves:
 //   - workgroup w owns a block of output rows for all k experts and wave j of
-//     it owns expert slot j: the wave loads its lane's columns of h_j first,
-//     then the down-projection rows of the block (so the h loads retire
-//     first), rescales h_j by a power of two into fp16 pairs, and computes
-//     each row's dot product; the block then sums the k weighted rows in
-//     ascending slot order and writes the output (or adds it to the residual).
+//     it owns expert slot j: the wave loads h_j (coalesced) and then the
+//     block's down-projection rows (so the h loads retire first); a row is
+//     spread over 16 lanes, four rows per wave load, so a row's partial sums
+//     meet in a four-step DPP reduction; the wave rescales h_j by a power of
+//     two into fp16 pairs once, into its own LDS region in lane-map order,
+//     and each lane reads the pairs of its columns from there; the block then
+//     sums the k weighted rows in ascending slot order and writes the output
+//     (or adds it to the residual).
 
 #pragma once
 
@@ -351,6 +354,11 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(D
 
 // --------------------------------------------------------------------- K2 --
 
+// K2 rows are spread over LPRD = 2^lg_d lanes (16 for the shapes built
+// here), so one wave load covers 64 / LPRD rows and a row's partial sums
+// meet in a short DPP reduction. Every lane of a row slot needs the same
+// columns of h_j, so the wave turns h_j into fp16 pairs once, in LDS, in
+// the lane-map order, and each lane reads its pairs from there.
 template <int BITS, typename ST, int VD, bool TBL>
 __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(DecodeArgs A) {
   constexpr int PPW = QT<BITS>::PPW;
@@ -359,9 +367,11 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(Deco
   using SPD = ScalePlan<BITS, VD>;
   // row loads per batch, two batches in flight
   constexpr int UDr = 32 / (VD + SPD::NS);
-  constexpr int UD = UDr < 1 ? 1 : (UDr > 8 ? 8 : UDr);
+  constexpr int UD = UDr < 1 ? 1 : (UDr > 4 ? 4 : UDr);
 
   __shared__ float s_part[SMOE_MAX_TOP_K * DEC_RB_MAX];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hp[DEC_WAVES][DEC_HP];
+  __shared__ float s_hk[DEC_WAVES][DEC_HW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = A.k;
@@ -372,7 +382,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(Deco
   const int r0 = (int)blockIdx.x * A.rb;
   int nrows = A.d - r0;
   nrows = nrows < 0 ? 0 : (nrows > A.rb ? A.rb : nrows);
-  const int upx = nrows / RPWD;  // row loads per expert
+  const int upx = (nrows + RPWD - 1) / RPWD;  // row loads per expert
   const int Wd = A.ffn * BITS / 32, Gd = A.ffn / 64;
   int sgd[SPD::NS], tmd;
   scale_groups<BITS, VD>(lrd, LPRD, sgd, tmd);
@@ -386,7 +396,8 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(Deco
 #pragma unroll
     for (int i = 0; i < UD; ++i) {
       const int ri = b0 + i < upx ? b0 + i : upx - 1;
-      const int row = r0 + ri * RPWD + rsd;
+      int row = r0 + ri * RPWD + rsd;
+      row = row < A.d ? row : A.d - 1;
       load_row_words<VD, true>(cbase + (size_t)row * Wd, lrd, LPRD, D.w[i]);
       load_row_scales<BITS, VD, ST, true>(sbase + (size_t)row * Gd, sgd, Gd, D.s[i]);
     }
@@ -397,67 +408,113 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_down(Deco
       if (b0 + i < upx) {  // wave-uniform
         float a = lane_row<BITS, VD, false>(D.w[i], H, D.s[i], tmd);
         a = seg_sum(a, lgd);
-        if (lrd == LPRD - 1) s_part[j * DEC_RB_MAX + (b0 + i) * RPWD + rsd] = a * H.oscale;
+        const int rl = (b0 + i) * RPWD + rsd;
+        if (lrd == LPRD - 1 && rl < nrows) s_part[j * DEC_RB_MAX + rl] = a * H.oscale;
       }
     }
   };
+  uint32_t* hp = s_hp[wave];
+  float* hk = s_hk[wave];
 #pragma unroll 1
   for (int j = wave; j < k && upx > 0; j += DEC_WAVES) {
     const int e = __builtin_amdgcn_readfirstlane(A.ws_ids[j]);
     const float wj = A.ws_w[j];
-    // h_j: the columns of this lane's VD code words, loaded first so they
-    // retire before the weight loads issued next
-    float hv[VD][WPW];
+    // h_j, code word c = lane + 64 t of it per lane (coalesced), loaded
+    // before the weights so that these loads retire first
     const float* hrow = A.h + (size_t)j * A.ffn;
+    float hv[DEC_HC][WPW];
 #pragma unroll
-    for (int w = 0; w < VD; ++w) {
-      const float* src = hrow + (size_t)LaneMap<VD>::word(lrd, LPRD, w) * WPW;
+    for (int t = 0; t < DEC_HC; ++t) {
+      const int c = lane + 64 * t;
+      const float* src = hrow + (size_t)(c < Wd ? c : Wd - 1) * WPW;
 #pragma unroll
       for (int i = 0; i < WPW / 4; ++i) {
         const f32x4 v = *(const f32x4*)(src + 4 * i);
-        hv[w][4 * i] = v.x;
-        hv[w][4 * i + 1] = v.y;
-        hv[w][4 * i + 2] = v.z;
-        hv[w][4 * i + 3] = v.w;
+        hv[t][4 * i] = v.x;
+        hv[t][4 * i + 1] = v.y;
+        hv[t][4 * i + 2] = v.z;
+        hv[t][4 * i + 3] = v.w;
       }
     }
     const uint8_t* blob = expert_blob(A.blobs, A.stride, TBL ? A.table : nullptr, e);
     const uint32_t* cbase = (const uint32_t*)(blob + A.dc);
     const ST* sbase = (const ST*)(blob + A.ds);
     issue_d(dA, 0, cbase, sbase);
-    // fp16 pairs of h_j, rescaled by a power of two (max over the segment,
-    // which holds the whole vector)
+    if (UD < upx) issue_d(dB, UD, cbase, sbase);
+    // fp16 pairs of h_j rescaled by a power of two (max over the vector),
+    // stored at the lane-map slot of each code word with the word's offset
     float m = 0.f;
 #pragma unroll
-    for (int w = 0; w < VD; ++w)
+    for (int t = 0; t < DEC_HC; ++t)
+      if (lane + 64 * t < Wd)
 #pragma unroll
-      for (int i = 0; i < WPW; ++i) m = fmaxf(m, fabsf(hv[w][i]));
-    m = lane63(seg_max(m, lgd));
+        for (int i = 0; i < WPW; ++i) m = fmaxf(m, fabsf(hv[t][i]));
+    m = lane63(seg_max(m, 6));
     const float S = pow2_prescale(m);
+    constexpr int N4 = LaneMap<VD>::N4, RT = LaneMap<VD>::R;
+#pragma unroll
+    for (int t = 0; t < DEC_HC; ++t) {
+      const int c = lane + 64 * t;
+      if (c < Wd) {
+        int lr, sl;
+        if (c < 4 * N4 * LPRD) {
+          const int ch = c / (4 * LPRD), rem = c - ch * 4 * LPRD;
+          lr = rem >> 2;
+          sl = 4 * ch + (rem & 3);
+        } else {
+          const int rem = c - 4 * N4 * LPRD;
+          lr = rem / (RT > 0 ? RT : 1);
+          sl = 4 * N4 + (rem - lr * (RT > 0 ? RT : 1));
+        }
+        float kk = 0.f;
+        uint32_t pw[PPW];
+#pragma unroll
+        for (int q = 0; q < PPW; ++q) {
+          const int hs = q / NPOS, pos = q % NPOS;
+          const int ia = hs * NPOS + pos, ib = ia + WPW / 2;
+          const float f = S * (1.0f / (float)(1 << (BITS * pos)));
+          const _Float16 ha = (_Float16)(hv[t][ia] * f), hb = (_Float16)(hv[t][ib] * f);
+          pw[q] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
+          kk = fmaf((float)ha + (float)hb, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)), kk);
+        }
+        uint32_t* dst = hp + (sl * LPRD + lr) * PPW;
+#pragma unroll
+        for (int q = 0; q < PPW; q += 4) *(u32x4*)(dst + q) = u32x4{pw[q], pw[q + 1], pw[q + 2], pw[q + 3]};
+        hk[sl * LPRD + lr] = kk;
+      }
+    }
+    // the wave's own LDS writes, read back by other lanes of the wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int w = 0; w < VD; ++w) {
-      float kk = 0.f;
+      const uint32_t* src = hp + (w * LPRD + lrd) * PPW;
 #pragma unroll
-      for (int q = 0; q < PPW; ++q) {
-        const int hs = q / NPOS, pos = q % NPOS;
-        const int ia = hs * NPOS + pos, ib = ia + WPW / 2;
-        const float f = S * (1.0f / (float)(1 << (BITS * pos)));
-        const _Float16 ha = (_Float16)(hv[w][ia] * f), hb = (_Float16)(hv[w][ib] * f);
-        H.hi[w][q] = f16x2{ha, hb};
-        kk = fmaf((float)ha + (float)hb, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)), kk);
+      for (int q = 0; q < PPW; q += 4) {
+        const u32x4 v = *(const u32x4*)(src + q);
+        // components to scalars before the bit casts (a bit cast of a
+        // vector component reads the vector's first element)
+        const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+        H.hi[w][q] = __builtin_bit_cast(f16x2, v0);
+        H.hi[w][q + 1] = __builtin_bit_cast(f16x2, v1);
+        H.hi[w][q + 2] = __builtin_bit_cast(f16x2, v2);
+        H.hi[w][q + 3] = __builtin_bit_cast(f16x2, v3);
       }
-      H.K[w] = kk;
+      H.K[w] = hk[w * LPRD + lrd];
     }
     fold_k(H);
     H.oscale = wj / (QT<BITS>::M * S);
 #pragma unroll 1
     for (int b0 = 0; b0 < upx; b0 += 2 * UD) {
-      if (b0 + UD < upx) issue_d(dB, b0 + UD, cbase, sbase);
       compute_d(dA, b0, j);
       if (b0 + UD >= upx) break;
       if (b0 + 2 * UD < upx) issue_d(dA, b0 + 2 * UD, cbase, sbase);
       compute_d(dB, b0 + UD, j);
+      if (b0 + 3 * UD < upx) issue_d(dB, b0 + 3 * UD, cbase, sbase);
     }
+    // the next expert slot of this wave rewrites the LDS pairs
+    __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
   if (tid < nrows) {

@@ -17,7 +17,9 @@ constexpr int DEC_WAVES_PER_EU = DEC_THREADS / 256;
 constexpr int DEC_RB_MAX = 64;     // down-projection rows per workgroup, max
 constexpr int DEC_XW = 4;          // x code words per thread (d * bits / 32 <= 4 * 512)
 constexpr int DEC_HJ = 2;          // h vectors staged per wave (k <= 16)
-constexpr int DEC_HC = 4;          // h code words per lane (Q4; half for Q2)
+constexpr int DEC_HC = 4;          // h code words per lane when a wave converts h_j (ffn * bits / 32 <= 256)
+constexpr int DEC_HW = 64 * DEC_HC;  // h code words per vector, max
+constexpr int DEC_HP = DEC_HW * 4;   // fp16 pairs of one h vector in LDS, max (Q4: 4 per word)
 constexpr int DEC_H_LDS = 12288;   // fp16 pairs of h held in LDS (k * ffn / 2 <= 12288)
 constexpr int DEC_KEYS = 512;      // routing keys in LDS, padding included
 
@@ -53,8 +55,8 @@ hipError_t launch_dec_down(const DecodeArgs& A, int nwg, hipStream_t s);
 
 // gate/up and down words-per-lane values with an instantiation
 #define SMOE_DEC_Q4_VG(X) X(8) X(4) X(1)
-#define SMOE_DEC_Q4_VD(X) X(3) X(11) X(1) X(5)
+#define SMOE_DEC_Q4_VD(X) X(12) X(11) X(8) X(6) X(4) X(2) X(1) X(16)
 #define SMOE_DEC_Q2_VG(X) X(4) X(2) X(1)
-#define SMOE_DEC_Q2_VD(X) X(3) X(11) X(1) X(5)
+#define SMOE_DEC_Q2_VD(X) X(6) X(11) X(8) X(4) X(2) X(1)
 
 }  // namespace smoe
