@@ -121,7 +121,7 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
   hipError_t e;
   {
     TracedLaunch t(SMOE_KERNEL_GATE_UP);
-    e = gu(A, DEC_NWG, stream);
+    e = gu(A, xf32 ? DEC_NWG : DEC_NWG_GU, stream);
   }
   if (e != hipSuccess) return e;
   {

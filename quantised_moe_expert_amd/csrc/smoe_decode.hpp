@@ -89,7 +89,8 @@ __device__ __forceinline__ float block_sum(float v, float* s_tmp) {
 // TBL: experts addressed through A.table (host offload); a template
 // parameter so that the resident-bank kernels carry no trace of it.
 template <int BITS, typename ST, int VG, bool XF32, bool TBL>
-__global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(DecodeArgs A) {
+__global__ __launch_bounds__(DEC_THREADS, XF32 ? DEC_WAVES_PER_EU : DEC_GU_WAVES_PER_EU) void k_dec_gate_up(
+    DecodeArgs A) {
   constexpr int PPW = QT<BITS>::PPW;
   constexpr int WPW = QT<BITS>::WPW;
   constexpr int NPOS = QT<BITS>::NPOS;
@@ -116,26 +117,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(D
   const int E = A.E, k = A.k;
   const int lgg = A.lg_g, LPRG = 1 << lgg, lrg = lane & (LPRG - 1), rsg = lane >> lgg;
 
-  // 1. loads: the x words this thread turns into fp16 pairs, and one logit
-  const int Wg = A.d * BITS / 32;
-  uint32_t xraw[DEC_XW][XRAW];
-  // slot t is used when t * DEC_THREADS < Wg (a workgroup-uniform test); the
-  // threads past Wg in the last slot load a valid word and ignore it
-#pragma unroll
-  for (int t = 0; t < DEC_XW; ++t) {
-    const int cw = tid + t * DEC_THREADS;
-    if (t * DEC_THREADS < Wg) {
-      const uint32_t* src = (const uint32_t*)A.x + (size_t)(cw < Wg ? cw : Wg - 1) * XRAW;
-#pragma unroll
-      for (int c = 0; c < XRAW / 4; ++c) {
-        const u32x4 v = *(const u32x4*)(src + 4 * c);
-        xraw[t][4 * c] = v.x;
-        xraw[t][4 * c + 1] = v.y;
-        xraw[t][4 * c + 2] = v.z;
-        xraw[t][4 * c + 3] = v.w;
-      }
-    }
-  }
+  // 1. loads: one logit, then the x words this thread turns into fp16 pairs
   float lv = -INFINITY;
   const int nkeys = 2 * A.rk_cp << A.rk_lg;
   if (tid < E) {
@@ -145,29 +127,23 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(D
     s_key[tid] = route_key(lv, tid);
   }
   for (int e = E + tid; e < nkeys; e += DEC_THREADS) s_key[e] = 0;
-  // one explicit wait for all of these loads in straight-line code: waits
-  // inserted inside the conditional blocks below would leave xraw "pending"
-  // at their joins, and the compiler would then wait for every outstanding
-  // load (the first weight batch included) where the pairs are built
-  __builtin_amdgcn_s_waitcnt(0);
-  float amax = 0.f, ssq = 0.f;
+  const int Wg = A.d * BITS / 32;
+  uint32_t xraw[DEC_XW][XRAW];
+  // slot t is used when t * DEC_THREADS < Wg; the loads are unconditional
+  // (threads past Wg load a valid word and ignore it), so waiting for them
+  // later does not also wait for the weight loads issued after them
 #pragma unroll
   for (int t = 0; t < DEC_XW; ++t) {
     const int cw = tid + t * DEC_THREADS;
-    if (t * DEC_THREADS < Wg) {
+    const uint32_t* src = (const uint32_t*)A.x + (size_t)(cw < Wg ? cw : Wg - 1) * XRAW;
 #pragma unroll
-      for (int i = 0; i < WPW; ++i) {
-        const float f = cw < Wg ? x_word_val<XF32>(xraw[t], i) : 0.f;
-        amax = fmaxf(amax, fabsf(f));
-        ssq = fmaf(f, f, ssq);
-      }
+    for (int c = 0; c < XRAW / 4; ++c) {
+      const u32x4 v = *(const u32x4*)(src + 4 * c);
+      xraw[t][4 * c] = v.x;
+      xraw[t][4 * c + 1] = v.y;
+      xraw[t][4 * c + 2] = v.z;
+      xraw[t][4 * c + 3] = v.w;
     }
-  }
-  amax = lane63(seg_max(amax, 6));
-  ssq = lane63(seg_sum(ssq, 6));
-  if (lane == 0) {
-    s_red[wave][0] = amax;
-    s_red[wave][1] = ssq;
   }
   __syncthreads();
 
@@ -219,11 +195,14 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(D
     uint32_t gw[UB][VG], uw[UB][VG];
     float gs[UB][SPG::NS], us[UB][SPG::NS];
   };
+  // a wave with no units reads row 0 of the first expert and ignores it:
+  // the first batch is requested unconditionally, so that later waits can
+  // count the loads exactly
   auto issue_b = [&](Batch& B, int b0) {
 #pragma unroll
     for (int i = 0; i < UB; ++i) {
       const int ui = b0 + i < my_n ? b0 + i : my_n - 1;
-      int rg = rg0 + ui;
+      int rg = my_n > 0 ? rg0 + ui : 0;
       const bool second = rg >= upe;
       rg = second ? rg - upe : rg;
       const int row = rg * RPWG + rsg;
@@ -239,10 +218,33 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_dec_gate_up(D
     }
   };
   Batch bA, bB;
-  if (my_n > 0) issue_b(bA, 0);
+  issue_b(bA, 0);
 
-  // 4. while the first batch is in flight: fp16 activation pairs and
-  //    offsets K, once per workgroup, into LDS
+  // 4. while the first batch is in flight: the maximum and the sum of
+  //    squares of x, then its fp16 activation pairs and offsets K, once per
+  //    workgroup, into LDS
+  {
+    float amax = 0.f, ssq = 0.f;
+#pragma unroll
+    for (int t = 0; t < DEC_XW; ++t) {
+      const int cw = tid + t * DEC_THREADS;
+      if (t * DEC_THREADS < Wg) {
+#pragma unroll
+        for (int i = 0; i < WPW; ++i) {
+          const float f = cw < Wg ? x_word_val<XF32>(xraw[t], i) : 0.f;
+          amax = fmaxf(amax, fabsf(f));
+          ssq = fmaf(f, f, ssq);
+        }
+      }
+    }
+    amax = lane63(seg_max(amax, 6));
+    ssq = lane63(seg_sum(ssq, 6));
+    if (lane == 0) {
+      s_red[wave][0] = amax;
+      s_red[wave][1] = ssq;
+    }
+  }
+  __syncthreads();
   float S, xos;
   {
     float m = 0.f, q = 0.f;

@@ -11,17 +11,22 @@ namespace smoe {
 
 constexpr int DEC_THREADS = 512;   // one workgroup of 8 waves per CU
 constexpr int DEC_NWG = 256;       // workgroups per launch (one per CU)
+constexpr int DEC_NWG_GU = 512;    // gate/up stage on bf16 inputs: two per CU (16 waves)
 // waves per SIMD the kernels are built for (HIP's second launch-bounds
 // argument): one 8-wave workgroup per CU
 constexpr int DEC_WAVES_PER_EU = DEC_THREADS / 256;
+// the gate/up stage on bf16 inputs runs two workgroups per CU: four waves per
+// SIMD, so at most 128 registers (fp32 inputs need the hi + lo pairs and keep
+// one workgroup per CU)
+constexpr int DEC_GU_WAVES_PER_EU = 2 * DEC_THREADS / 256;
 constexpr int DEC_RB_MAX = 64;     // down-projection rows per workgroup, max
 constexpr int DEC_XW = 4;          // x code words per thread (d * bits / 32 <= 4 * 512)
 constexpr int DEC_HJ = 2;          // h vectors staged per wave (k <= 16)
 constexpr int DEC_HC = 4;          // h code words per lane when a wave converts h_j (ffn * bits / 32 <= 256)
 constexpr int DEC_HW = 64 * DEC_HC;  // h code words per vector, max
 constexpr int DEC_HP = DEC_HW * 4;   // fp16 pairs of one h vector in LDS, max (Q4: 4 per word)
-constexpr int DEC_H_LDS = 12288;   // fp16 pairs of h held in LDS (k * ffn / 2 <= 12288)
 constexpr int DEC_KEYS = 512;      // routing keys in LDS, padding included
+constexpr int DEC_H_LDS = 12288;   // fp16 pairs of h held in LDS (k * ffn / 2 <= 12288)
 
 struct DecodeArgs {
   const uint8_t* blobs;  // routed expert bank, expert e at blobs + e * stride
