@@ -102,23 +102,6 @@ __device__ __forceinline__ float seg_max(float v, int lg) {
   return v;
 }
 
-// Maximum of an unsigned value over the whole wave, returned to every lane
-// (0 is the identity: lanes whose DPP source is off the row read 0).
-template <int CTRL, int RMASK>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, RMASK, 0xF, false);
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
-  v = max(v, dpp_u32<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
-  v = max(v, dpp_u32<0x141, 0xF>(v));  // row_half_mirror
-  v = max(v, dpp_u32<0x140, 0xF>(v));  // row_mirror
-  v = max(v, dpp_u32<0x142, 0xA>(v));  // row_bcast15 into rows 1, 3
-  v = max(v, dpp_u32<0x143, 0xC>(v));  // row_bcast31 into rows 2, 3
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
 __device__ __forceinline__ float lane63(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
