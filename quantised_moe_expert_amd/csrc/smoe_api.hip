@@ -214,6 +214,29 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
       return rc;
     if (launched) return SMOE_OK;
   }
+  if (T >= 2 && cfg.is_default()) {
+    // a few tokens: routing, grouping and gate/up in one launch, then the
+    // grouped down stage and the combine
+    bool launched = false;
+    if ((rc = check_hip(small_try(L, x, xmode != X_BF16, xmode == X_F32_RMS, eps, logits, T, k,
+                                  norm, nsh, uids, uw, ids, w, meta, active, offs, pair_token,
+                                  pair_of, h, s, &launched),
+                        "small-batch gate/up launch")))
+      return rc;
+    if (launched) {
+      float* ysh = nsh ? y + (size_t)T * k * L.desc.d_model : nullptr;
+      {
+        TracedLaunch t(SMOE_KERNEL_DOWN);
+        rc = check_hip(launch_down(L, false, h, T, pairs, max_slots, meta, active, offs, y, s,
+                                   nullptr, nsh),
+                       "down launch");
+      }
+      if (rc) return rc;
+      return check_hip(launch_combine(y, pair_of, w, ysh, nsh ? nsh : 1, nullptr, out, T, k,
+                                      (int)L.desc.d_model, accumulate, s),
+                       "combine launch");
+    }
+  }
   // the shared expert needs only x: it runs on the layer's side stream from
   // the work enqueued so far, beside routing and the routed stages, and the
   // combine waits for it

@@ -55,6 +55,40 @@ bool find_pair(int bits, int sdt, int vg, int vd, bool xf32, GuLaunch* G, DnLaun
   return find_gu<2, _Float16>(vg, xf32, G) && find_dn<2, _Float16>(vd, D);
 }
 
+typedef hipError_t (*SbLaunch)(const SmallArgs&, int, hipStream_t);
+
+template <int BITS, typename ST>
+bool find_sb(int vg, bool xf32, SbLaunch* L) {
+#define SMOE_FIND_SB(v)                                                       \
+  if (vg == v) {                                                             \
+    *L = xf32 ? launch_sb_gate_up<BITS, ST, v, true>                         \
+              : launch_sb_gate_up<BITS, ST, v, false>;                       \
+    return true;                                                             \
+  }
+  if constexpr (BITS == 4) {
+    SMOE_DEC_Q4_VG(SMOE_FIND_SB)
+  } else {
+    SMOE_DEC_Q2_VG(SMOE_FIND_SB)
+  }
+#undef SMOE_FIND_SB
+  return false;
+}
+
+bool find_sb_any(int bits, int sdt, int vg, bool xf32, SbLaunch* L) {
+  if (bits == 4 && sdt == SMOE_SCALE_F32) return find_sb<4, float>(vg, xf32, L);
+  if (bits == 4) return find_sb<4, _Float16>(vg, xf32, L);
+  if (sdt == SMOE_SCALE_F32) return find_sb<2, float>(vg, xf32, L);
+  return find_sb<2, _Float16>(vg, xf32, L);
+}
+
+uint64_t align16(uint64_t v) { return (v + 15) / 16 * 16; }
+
+// static LDS of k_sb_gate_up: expert masks, slots, active list, offsets,
+// selections (see smoe_small.hpp)
+constexpr uint64_t SB_STATIC_LDS = (4ull * SMOE_MAX_EXPERTS + 1) * 4 +
+                                   2ull * SB_TSLOTS * SMOE_MAX_TOP_K * 4 + 64 +
+                                   (DEC_THREADS / 64) * 64 * 4;
+
 }  // namespace
 
 hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, float eps,
@@ -127,6 +161,79 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
   {
     TracedLaunch t(SMOE_KERNEL_DOWN);
     e = dn(A, DEC_NWG, stream);
+  }
+  if (e != hipSuccess) return e;
+  *launched = true;
+  return hipSuccess;
+}
+
+hipError_t small_try(const LayerInfo& L, const void* x, bool xf32, bool rms, float eps,
+                     const float* logits, int T, int k, int norm, int nsh, int32_t* uids,
+                     float* uw, int32_t* ids, float* w, int* meta, int* active, int* offs,
+                     int* pair_token, int* pair_of, float* h, hipStream_t stream,
+                     bool* launched) {
+  *launched = false;
+  const ExpertPlan& P = L.plan;
+  const int E = (int)L.desc.num_experts, bits = (int)L.desc.bits;
+  if (T < 2 || T > SB_TMAX || (int64_t)T * E > SB_KEYS) return hipSuccess;
+  if (L.desc.shared_ffn_dim && nsh <= 0) return hipSuccess;
+  // a unit's results (tokens x rows per wave load) are staged in 64 floats
+  if (T * (64 >> P.gate.lpr_log2) > 64) return hipSuccess;
+  SbLaunch sb;
+  if (!find_sb_any(bits, (int)L.desc.scale_dtype, P.gate.v, xf32, &sb)) return hipSuccess;
+  // dynamic LDS: keys, logits, fp16 pairs (hi, and lo for fp32 inputs), offsets
+  const int ppw = 16 / bits;
+  const uint64_t xpt = (uint64_t)P.gate.v * ppw * 64;
+  SmallArgs A{};
+  A.lds_lv = (int)align16((uint64_t)T * E * 8);
+  A.lds_xp = (int)align16(A.lds_lv + (uint64_t)T * E * 4);
+  A.lds_k = (int)align16(A.lds_xp + (uint64_t)T * (xf32 ? 2 : 1) * xpt * 4);
+  A.lds_os = (int)align16(A.lds_k + (uint64_t)T * P.gate.v * 64 * 4);
+  A.lds_total = (int)align16(A.lds_os + (uint64_t)T * 4);
+  // two workgroups per CU when both fit the 160 KB of LDS (bf16 inputs)
+  const uint64_t per_wg = A.lds_total + SB_STATIC_LDS;
+  if (per_wg > 150 * 1024) return hipSuccess;
+  const int nwg = !xf32 && per_wg <= 78 * 1024 ? DEC_NWG_GU : DEC_NWG;
+  A.blobs = L.blobs;
+  A.stride = L.desc.blob_stride;
+  A.table = L.table;
+  A.gc = P.gate.codes_off;
+  A.gs = P.gate.scales_off;
+  A.uc = P.up.codes_off;
+  A.us = P.up.scales_off;
+  if (nsh) {
+    A.shared = L.shared;
+    A.sgc = L.shared_plan.gate.codes_off;
+    A.sgs = L.shared_plan.gate.scales_off;
+    A.suc = L.shared_plan.up.codes_off;
+    A.sus = L.shared_plan.up.scales_off;
+  }
+  A.d = P.d_model;
+  A.ffn = P.ffn;
+  A.E = E;
+  A.k = k;
+  A.T = T;
+  A.norm = norm;
+  A.nsh = nsh;
+  A.lg_g = P.gate.lpr_log2;
+  A.x = x;
+  A.rms = rms ? 1 : 0;
+  A.eps = eps;
+  A.logits = logits;
+  A.h = h;
+  A.ids = ids;
+  A.w = w;
+  A.meta = meta;
+  A.active = active;
+  A.offs = offs;
+  A.pair_token = pair_token;
+  A.pair_of = pair_of;
+  A.user_ids = uids;
+  A.user_w = uw;
+  hipError_t e;
+  {
+    TracedLaunch t(SMOE_KERNEL_GATE_UP);
+    e = sb(A, nwg, stream);
   }
   if (e != hipSuccess) return e;
   *launched = true;

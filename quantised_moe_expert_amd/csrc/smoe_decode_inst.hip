@@ -2,6 +2,7 @@
 // scale type) with -DSMOE_INST_BITS and -DSMOE_INST_ST.
 
 #include "smoe_decode.hpp"
+#include "smoe_small.hpp"
 
 #ifndef SMOE_INST_BITS
 #error "SMOE_INST_BITS not set"
@@ -13,7 +14,11 @@ namespace smoe {
   template hipError_t launch_dec_gate_up<SMOE_INST_BITS, SMOE_INST_ST, vg, false>(           \
       const DecodeArgs&, int, hipStream_t);                                                   \
   template hipError_t launch_dec_gate_up<SMOE_INST_BITS, SMOE_INST_ST, vg, true>(            \
-      const DecodeArgs&, int, hipStream_t);
+      const DecodeArgs&, int, hipStream_t);                                                   \
+  template hipError_t launch_sb_gate_up<SMOE_INST_BITS, SMOE_INST_ST, vg, false>(            \
+      const SmallArgs&, int, hipStream_t);                                                    \
+  template hipError_t launch_sb_gate_up<SMOE_INST_BITS, SMOE_INST_ST, vg, true>(             \
+      const SmallArgs&, int, hipStream_t);
 #define SMOE_DEC_INST_D(vd)                                                                  \
   template hipError_t launch_dec_down<SMOE_INST_BITS, SMOE_INST_ST, vd>(const DecodeArgs&,  \
                                                                          int, hipStream_t);

@@ -131,6 +131,17 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
                        int32_t* uids, float* uw, float* h, int32_t* ws_ids, float* ws_w,
                        hipStream_t stream, bool* launched);
 
+// Small batches (2..16 tokens): routing, grouping and the gate/up stage in one
+// launch, writing ids, w, meta, active, offs, pair_token, pair_of and h in the
+// grouped layout the down stage and the combine read; nsh as for the grouped
+// stages (the shared expert's parts after the routed pairs). Sets *launched =
+// false (and enqueues nothing) when the call does not fit this path.
+hipError_t small_try(const LayerInfo& L, const void* x, bool xf32, bool rms, float eps,
+                     const float* logits, int T, int k, int norm, int nsh, int32_t* uids,
+                     float* uw, int32_t* ids, float* w, int* meta, int* active, int* offs,
+                     int* pair_token, int* pair_of, float* h, hipStream_t stream,
+                     bool* launched);
+
 // y_shared (nullable): nsh partial outputs of the shared expert, [nsh][T][d],
 // summed; shared_gate (nullable, [T] logits): the shared expert's weight is
 // sigmoid(shared_gate[t]) instead of 1.

@@ -1,0 +1,429 @@
+// Small batches (2..4 tokens) on gfx950: routing, grouping and the gate/up
+// stage in one launch, the one-token design extended to a few tokens.
+//
+// Every workgroup routes all T tokens itself ("CMF v2 Format Specification",
+// 2.2 MoE: top-k of the logits, equal logits to the lower expert id,
+// softmax-over-all weights, renormalised on request) by counting, for each
+// (token, expert), the token's logits above its own; it then groups the
+// selections by expert in LDS (a token bitmask per expert, a scan over the
+// experts) in the grouped layout the down stage and the combine read: active
+// experts ascending, inside an expert the tokens ascending, the shared
+// expert's parts after the routed pairs (pair P + v T + t). Workgroup 0
+// publishes that layout. The gate/up rows of every active expert (and of the
+// shared expert's parts) are then split evenly over all waves, each row read
+// once and dotted with every token that selected the expert, from fp16
+// activation pairs built once per workgroup in LDS; SwiGLU is fused and h is
+// stored per grouped pair.
+
+#pragma once
+
+#include "smoe_decode.hpp"
+
+namespace smoe {
+
+// Four waves per SIMD (two workgroups per CU, 128 registers) when a lane
+// holds at most 16 activation pairs of a token and the input is bf16; else two.
+template <int BITS, int VG, bool XF32>
+constexpr bool sb_narrow() {
+  return !XF32 && VG * QT<BITS>::PPW <= 16;
+}
+
+// tokens per wave when building the activation pairs (wave w takes w, w + 8, ...)
+constexpr int SB_XSLOTS = (SB_TMAX + DEC_WAVES - 1) / DEC_WAVES;
+
+template <int BITS, typename ST, int VG, bool XF32>
+__global__ __launch_bounds__(DEC_THREADS, (sb_narrow<BITS, VG, XF32>() ? DEC_GU_WAVES_PER_EU
+                                                                       : DEC_WAVES_PER_EU)) void
+k_sb_gate_up(SmallArgs A) {
+  constexpr int PPW = QT<BITS>::PPW;
+  constexpr int WPW = QT<BITS>::WPW;
+  constexpr int NPOS = QT<BITS>::NPOS;
+  constexpr bool SPLIT = XF32;
+  using SPG = ScalePlan<BITS, VG>;
+  constexpr int UBr = (SPLIT ? 36 : 24) / (2 * (VG + SPG::NS));
+  constexpr int UB = UBr < 1 ? 1 : (UBr > 2 ? 2 : UBr);  // row pairs per batch
+  constexpr int XRAW = XF32 ? WPW : WPW / 2;             // 32-bit words of x per code word
+  constexpr int XPT = VG * PPW * 64;                     // fp16-pair words of one token
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint64_t* s_key = (uint64_t*)smem;                      // [T * E]
+  float* s_lv = (float*)(smem + A.lds_lv);                // [T * E]
+  uint32_t* s_xp = (uint32_t*)(smem + A.lds_xp);          // [T][(SPLIT ? 2 : 1) * XPT]
+  float* s_K = (float*)(smem + A.lds_k);                  // [T][VG * 64]
+  float* s_os = (float*)(smem + A.lds_os);                // [T]
+  __shared__ uint32_t s_mask[SMOE_MAX_EXPERTS];           // tokens that selected expert e
+  __shared__ int s_slot[SMOE_MAX_EXPERTS];                // slot of expert e
+  __shared__ int s_act[SMOE_MAX_EXPERTS];                 // expert of slot s
+  __shared__ int s_off[SMOE_MAX_EXPERTS + 1];             // first grouped pair of slot s
+  __shared__ int s_sel[SB_TSLOTS * SMOE_MAX_TOP_K];         // selection j of token t
+  __shared__ float s_val[SB_TSLOTS * SMOE_MAX_TOP_K];       // its logit
+  __shared__ int s_scan[DEC_WAVES];
+  __shared__ int s_nact;
+  __shared__ float s_hout[DEC_WAVES][64];                 // a unit's results before the store
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = A.T, E = A.E, k = A.k, nsh = A.nsh;
+  const int TE = T * E, P = T * k;
+
+  // 1. routing keys: (token, expert) -> key ordering larger logits first,
+  //    equal logits by ascending expert id
+  for (int i = tid; i < TE; i += DEC_THREADS) {
+    float f = A.logits[i];
+    if (f != f) f = -INFINITY;  // NaN never outranks a number
+    s_lv[i] = f;
+    s_key[i] = route_key(f, i % E);
+  }
+  for (int e = tid; e < E; e += DEC_THREADS) s_mask[e] = 0u;
+  __syncthreads();
+
+  // 2. rank of each (token, expert) among the token's keys; the k lowest are
+  //    its selection
+  for (int i = tid; i < TE; i += DEC_THREADS) {
+    const int t = i / E, e = i - t * E;
+    const uint64_t ki = s_key[i];
+    const uint64_t* row = s_key + (size_t)t * E;
+    int cnt = 0;
+    for (int j = 0; j < E; ++j) cnt += (int)(row[j] > ki);
+    if (cnt < k) {
+      s_sel[t * k + cnt] = e;
+      s_val[t * k + cnt] = s_lv[i];
+      atomicOr(&s_mask[e], 1u << t);
+    }
+  }
+  __syncthreads();
+
+  // 3. grouping: a scan over the experts of (active, tokens) gives each
+  //    active expert its slot and its first grouped pair
+  {
+    int na = 0, np = 0;  // running totals over earlier blocks of 512 experts
+    for (int base = 0; base < E; base += DEC_THREADS) {
+      const int e = base + tid;
+      const uint32_t m = e < E ? s_mask[e] : 0u;
+      const int v = m ? (1 << 16) + __popc(m) : 0;  // active count | pair count
+      int x = v;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) s_scan[wave] = x;
+      __syncthreads();
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < DEC_WAVES; ++w) {
+        const int sw = s_scan[w];
+        pre += w < wave ? sw : 0;
+        tot += sw;
+      }
+      const int excl = pre + x - v;
+      if (m) {
+        const int s = na + (excl >> 16);
+        s_slot[e] = s;
+        s_act[s] = e;
+        s_off[s] = np + (excl & 0xFFFF);
+      }
+      na += tot >> 16;
+      np += tot & 0xFFFF;
+      __syncthreads();
+    }
+    if (tid == 0) s_nact = na;
+  }
+  __syncthreads();
+  const int nact = s_nact;
+
+  // 4. this wave's units: (slot, row group) over the shared expert's parts
+  //    first (all T tokens each), then the active experts, split evenly over
+  //    all waves; a wave's units span at most two slots
+  const int lgg = A.lg_g, LPRG = 1 << lgg, lrg = lane & (LPRG - 1), rsg = lane >> lgg;
+  const int RPWG = 64 >> lgg;
+  const int upe = A.ffn / RPWG;
+  const int nq = nsh + nact;
+  const int units = nq * upe;
+  const int TW = (int)gridDim.x * DEC_WAVES, gw = (int)blockIdx.x * DEC_WAVES + wave;
+  const int ub = units / TW, urem = units % TW;
+  const int my_n = ub + (gw < urem ? 1 : 0);
+  const int u0 = gw * ub + (gw < urem ? gw : urem);
+  const int q0 = my_n > 0 ? u0 / upe : 0;
+  const int rg0 = u0 - q0 * upe;
+  const int Wg = A.d * BITS / 32, Gg = A.d / 64;
+  int sgg[SPG::NS], tmg;
+  scale_groups<BITS, VG>(lrg, LPRG, sgg, tmg);
+  // unit q: its matrices' first row, its tokens and its first grouped pair
+  struct Unit {
+    const uint32_t *gc, *uc;
+    const ST *gs, *us;
+    uint32_t tm;
+    int pb;
+  };
+  auto unit = [&](int q) {
+    Unit U;
+    const uint8_t* b;
+    uint64_t row0;
+    if (q < nsh) {
+      b = A.shared;
+      row0 = (uint64_t)q * A.ffn;
+      U.gc = (const uint32_t*)(b + A.sgc) + row0 * Wg;
+      U.uc = (const uint32_t*)(b + A.suc) + row0 * Wg;
+      U.gs = (const ST*)(b + A.sgs) + row0 * Gg;
+      U.us = (const ST*)(b + A.sus) + row0 * Gg;
+      U.tm = T >= 32 ? 0xFFFFFFFFu : (1u << T) - 1u;
+      U.pb = P + q * T;
+    } else {
+      const int s = q - nsh < nact ? q - nsh : 0;
+      b = expert_blob(A.blobs, A.stride, A.table, s_act[s]);
+      U.gc = (const uint32_t*)(b + A.gc);
+      U.uc = (const uint32_t*)(b + A.uc);
+      U.gs = (const ST*)(b + A.gs);
+      U.us = (const ST*)(b + A.us);
+      U.tm = s_mask[s_act[s]];
+      U.pb = s_off[s];
+    }
+    return U;
+  };
+  const Unit U0 = unit(q0);
+  const Unit U1 = unit(q0 + 1 < nq ? q0 + 1 : q0);
+  struct Batch {
+    uint32_t gw[UB][VG], uw[UB][VG];
+    float gs[UB][SPG::NS], us[UB][SPG::NS];
+  };
+  // a wave with no units reads row 0 of its first unit and ignores it: the
+  // first batch is requested unconditionally, so that later waits count the
+  // loads exactly
+  auto issue_b = [&](Batch& B, int b0) {
+#pragma unroll
+    for (int i = 0; i < UB; ++i) {
+      const int ui = b0 + i < my_n ? b0 + i : my_n - 1;
+      int rg = my_n > 0 ? rg0 + ui : 0;
+      const bool second = rg >= upe;
+      rg = second ? rg - upe : rg;
+      const int row = rg * RPWG + rsg;
+      const Unit& Uu = second ? U1 : U0;
+      load_row_words<VG, true>(Uu.gc + (size_t)row * Wg, lrg, LPRG, B.gw[i]);
+      load_row_words<VG, true>(Uu.uc + (size_t)row * Wg, lrg, LPRG, B.uw[i]);
+      load_row_scales<BITS, VG, ST, true>(Uu.gs + (size_t)row * Gg, sgg, Gg, B.gs[i]);
+      load_row_scales<BITS, VG, ST, true>(Uu.us + (size_t)row * Gg, sgg, Gg, B.us[i]);
+    }
+  };
+  // the x words of this wave's token (wave w takes token w), requested before the
+  // weights so that they retire first; the loads are unconditional (a
+  // missing token reads the last one, a missing word the row's last)
+  uint32_t xr[SB_XSLOTS][VG][XRAW];
+#pragma unroll
+  for (int tt = 0; tt < SB_XSLOTS; ++tt) {
+    const int tr = wave + tt * DEC_WAVES;
+    const uint32_t* xt = (const uint32_t*)A.x + (size_t)(tr < T ? tr : T - 1) * Wg * XRAW;
+#pragma unroll
+    for (int i = 0; i < VG; ++i) {
+      const int cw = lane + 64 * i;
+      const uint32_t* src = xt + (size_t)(cw < Wg ? cw : Wg - 1) * XRAW;
+#pragma unroll
+      for (int c = 0; c < XRAW / 4; ++c) {
+        const u32x4 v = *(const u32x4*)(src + 4 * c);
+        xr[tt][i][4 * c] = v.x;
+        xr[tt][i][4 * c + 1] = v.y;
+        xr[tt][i][4 * c + 2] = v.z;
+        xr[tt][i][4 * c + 3] = v.w;
+      }
+    }
+  }
+  Batch bA, bB;
+  issue_b(bA, 0);
+
+  // 5. workgroup 0 publishes the selection, the weights and the grouped
+  //    layout; wave w takes token w
+  if (blockIdx.x == 0) {
+    for (int t = wave; t < T; t += DEC_WAVES) {
+      const float mx = s_val[t * k];
+      float se = 0.f;
+      for (int e = lane; e < E; e += 64) se += expf(s_lv[t * E + e] - mx);
+      se = lane63(seg_sum(se, 6));
+      const float p = lane < k ? expf(s_val[t * k + (lane < k ? lane : 0)] - mx) / se : 0.f;
+      const float psum = lane63(seg_sum(p, 6));
+      if (lane < k) {
+        const int e = s_sel[t * k + lane];
+        const float wt = A.norm ? p / psum : p;
+        const int o = t * k + lane;
+        const int pos = s_off[s_slot[e]] + __popc(s_mask[e] & ((1u << t) - 1u));
+        A.ids[o] = e;
+        A.w[o] = wt;
+        A.pair_of[o] = pos;
+        A.pair_token[pos] = t;
+        if (A.user_ids) A.user_ids[o] = e;
+        if (A.user_w) A.user_w[o] = wt;
+      }
+    }
+    for (int s = tid; s < nact; s += DEC_THREADS) {
+      A.active[s] = s_act[s];
+      A.offs[s] = s_off[s];
+    }
+    for (int v = tid; v <= nsh; v += DEC_THREADS) A.offs[nact + v] = P + v * T;
+    for (int i = tid; i < nsh * T; i += DEC_THREADS) A.pair_token[P + i] = i % T;
+    if (tid == 0) {
+      A.meta[0] = nact;
+      A.meta[1] = P;
+    }
+  }
+
+  // 6. fp16 activation pairs and offsets K of every token, built once per
+  //    workgroup in LDS from the words loaded in step 4 (wave w takes token w)
+#pragma unroll
+  for (int tt = 0; tt < SB_XSLOTS; ++tt) {
+    const int tr = wave + tt * DEC_WAVES;
+    const int t = tr < T ? tr : T - 1;
+    if (tr < T) {  // wave-uniform
+      float amax = 0.f, ssq = 0.f;
+#pragma unroll
+      for (int i = 0; i < VG; ++i) {
+        if (lane + 64 * i < Wg) {
+#pragma unroll
+          for (int j = 0; j < WPW; ++j) {
+            const float f = x_word_val<XF32>(xr[tt][i], j);
+            amax = fmaxf(amax, fabsf(f));
+            ssq = fmaf(f, f, ssq);
+          }
+        }
+      }
+      amax = lane63(seg_max(amax, 6));
+      ssq = lane63(seg_sum(ssq, 6));
+      const float S = pow2_prescale(amax);
+      const float rr = A.rms ? 1.0f / sqrtf(ssq / (float)A.d + A.eps) : 1.0f;
+      if (lane == 0) s_os[t] = rr / (QT<BITS>::M * S);
+      uint32_t* xp = s_xp + (size_t)t * (SPLIT ? 2 : 1) * XPT;
+      float* kt = s_K + (size_t)t * VG * 64;
+#pragma unroll
+      for (int i = 0; i < VG; ++i) {
+        const int cw = lane + 64 * i;
+        if (cw < Wg) {
+          // lane lr and slot w holding code word cw (inverse of LaneMap)
+          constexpr int N4 = LaneMap<VG>::N4, RT = LaneMap<VG>::R;
+          int lr, w;
+          if (cw < 4 * N4 * LPRG) {
+            const int c = cw / (4 * LPRG), rem = cw - c * 4 * LPRG;
+            lr = rem >> 2;
+            w = 4 * c + (rem & 3);
+          } else {
+            const int rem = cw - 4 * N4 * LPRG;
+            lr = rem / (RT > 0 ? RT : 1);
+            w = 4 * N4 + (rem - lr * (RT > 0 ? RT : 1));
+          }
+          float kk = 0.f;
+          uint32_t ph[PPW], pl[PPW];
+#pragma unroll
+          for (int q = 0; q < PPW; ++q) {
+            const int hs = q / NPOS, pos = q % NPOS;
+            const int ia = hs * NPOS + pos, ib = ia + WPW / 2;
+            const float f = S * (1.0f / (float)(1 << (BITS * pos)));
+            const float a = x_word_val<XF32>(xr[tt][i], ia) * f;
+            const float b = x_word_val<XF32>(xr[tt][i], ib) * f;
+            const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+            ph[q] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
+            float sumx = (float)ha + (float)hb;
+            if constexpr (SPLIT) {
+              const _Float16 la = (_Float16)(a - (float)ha), lb = (_Float16)(b - (float)hb);
+              pl[q] = __builtin_bit_cast(uint32_t, f16x2{la, lb});
+              sumx += (float)la + (float)lb;
+            } else {
+              pl[q] = 0u;
+            }
+            kk = fmaf(sumx, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)), kk);
+          }
+          uint32_t* dst = xp + (w * LPRG + lr) * PPW;
+#pragma unroll
+          for (int q = 0; q < PPW; q += 4) {
+            *(u32x4*)(dst + q) = u32x4{ph[q], ph[q + 1], ph[q + 2], ph[q + 3]};
+            if constexpr (SPLIT)
+              *(u32x4*)(dst + XPT + q) = u32x4{pl[q], pl[q + 1], pl[q + 2], pl[q + 3]};
+          }
+          kt[w * LPRG + lr] = kk;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // 7. gate/up dot products for every token of a unit, SwiGLU, h per pair;
+  //    the next batch's loads are issued before the current batch is computed
+  auto load_x = [&](int t, XRegs<BITS, VG, SPLIT>& X) {
+    const uint32_t* xp = s_xp + (size_t)t * (SPLIT ? 2 : 1) * XPT;
+#pragma unroll
+    for (int w = 0; w < VG; ++w) {
+#pragma unroll
+      for (int q = 0; q < PPW; q += 4) {
+        const u32x4 v = *(const u32x4*)(xp + (w * LPRG + lrg) * PPW + q);
+        // components to scalars before the bit casts (a bit cast of a
+        // vector component reads the vector's first element)
+        const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+        X.hi[w][q] = __builtin_bit_cast(f16x2, v0);
+        X.hi[w][q + 1] = __builtin_bit_cast(f16x2, v1);
+        X.hi[w][q + 2] = __builtin_bit_cast(f16x2, v2);
+        X.hi[w][q + 3] = __builtin_bit_cast(f16x2, v3);
+        if constexpr (SPLIT) {
+          const u32x4 l = *(const u32x4*)(xp + XPT + (w * LPRG + lrg) * PPW + q);
+          const uint32_t l0 = l.x, l1 = l.y, l2 = l.z, l3 = l.w;
+          X.lo[w][q] = __builtin_bit_cast(f16x2, l0);
+          X.lo[w][q + 1] = __builtin_bit_cast(f16x2, l1);
+          X.lo[w][q + 2] = __builtin_bit_cast(f16x2, l2);
+          X.lo[w][q + 3] = __builtin_bit_cast(f16x2, l3);
+        }
+      }
+      X.K[w] = s_K[(size_t)t * VG * 64 + w * LPRG + lrg];
+    }
+    X.oscale = s_os[t];
+    fold_k(X);
+  };
+  auto compute_b = [&](const Batch& B, int b0) {
+#pragma unroll
+    for (int i = 0; i < UB; ++i) {
+      int rg = rg0 + b0 + i;
+      const bool second = rg >= upe;
+      rg = second ? rg - upe : rg;
+      const Unit& Uu = second ? U1 : U0;
+      uint32_t m = b0 + i < my_n ? Uu.tm : 0u;  // wave-uniform
+      // the results go to LDS inside the token loop and to h in one store
+      // after it: a global store inside a loop of unknown trip count would
+      // make the compiler wait for every outstanding load (the next batch
+      // included) before the loop
+      int rank = 0;
+      while (m) {
+        const int t = __builtin_ctz(m);
+        m &= m - 1u;
+        XRegs<BITS, VG, SPLIT> X;
+        load_x(t, X);
+        float ag = lane_row<BITS, VG, SPLIT>(B.gw[i], X, B.gs[i], tmg);
+        float au = lane_row<BITS, VG, SPLIT>(B.uw[i], X, B.us[i], tmg);
+        ag = seg_sum(ag, lgg);
+        au = seg_sum(au, lgg);
+        if (lrg == LPRG - 1) {
+          const float g = ag * X.oscale, uu = au * X.oscale;
+          s_hout[wave][rank * RPWG + rsg] = g / (1.0f + expf(-g)) * uu;
+        }
+        ++rank;
+      }
+      if (lane < rank * RPWG)
+        A.h[(size_t)(Uu.pb + lane / RPWG) * A.ffn + rg * RPWG + lane % RPWG] = s_hout[wave][lane];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int b0 = 0; b0 < my_n; b0 += 2 * UB) {
+    if (b0 + UB < my_n) issue_b(bB, b0 + UB);
+    compute_b(bA, b0);
+    if (b0 + UB >= my_n) break;
+    if (b0 + 2 * UB < my_n) issue_b(bA, b0 + 2 * UB);
+    compute_b(bB, b0 + UB);
+  }
+}
+
+// nwg: DEC_NWG_GU when the caller's LDS budget allows two workgroups per CU
+// (reduced to DEC_NWG for the instantiations built for one)
+template <int BITS, typename ST, int VG, bool XF32>
+hipError_t launch_sb_gate_up(const SmallArgs& A, int nwg, hipStream_t s) {
+  if (!sb_narrow<BITS, VG, XF32>()) nwg = DEC_NWG;
+  auto kernel = k_sb_gate_up<BITS, ST, VG, XF32>;
+  if (A.lds_total > 65536) {  // workgroups of more than 64 KB of LDS need the limit raised
+    const hipError_t e = hipFuncSetAttribute(
+        (const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, A.lds_total);
+    if (e != hipSuccess) return e;
+  }
+  return launch_kernel_lds(kernel, dim3(nwg), dim3(DEC_THREADS), (unsigned)A.lds_total, s, A);
+}
+
+}  // namespace smoe

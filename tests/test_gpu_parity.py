@@ -132,6 +132,46 @@ def test_small_layers(case, x_dtype):
     _check_layer(hl, x, lg, k, norm, x_dtype)
 
 
+# Two to four tokens take the small-batch path: routing and grouping inside
+# the gate/up launch (every workgroup), the grouped layout published by the
+# first workgroup, then the grouped down stage and the combine.
+SMALL_BATCH = [
+    # d, ffn, E, k, T, bits, scales, norm, shared
+    (4096, 1536, 128, 8, 3, 4, "f32", True, 0),
+    (1024, 256, 512, 16, 4, 4, "f16", True, 768),
+    (512, 320, 16, 16, 2, 2, "f32", True, 640),
+    (2048, 1408, 64, 6, 4, 4, "f32", False, 2816),
+    (768, 192, 40, 7, 4, 2, "f16", False, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_BATCH,
+                         ids=[f"d{c[0]}_f{c[1]}_E{c[2]}_k{c[3]}_T{c[4]}_q{c[5]}_{c[6]}"
+                              f"_n{int(c[7])}_s{c[8]}" for c in SMALL_BATCH])
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_small_batch_path(case, x_dtype):
+    _torch()
+    d, ffn, E, k, T, bits, sd, norm, shared = case
+    hl = random_layer(3100 + d + E + T, d, ffn, E, bits, sd, shared)
+    r = synth.rng(3200 + T + E)
+    x = _x(r, T, d, x_dtype)
+    lg = synth.normal_f32(r, (T, E))
+    _check_layer(hl, x, lg, k, norm, x_dtype)
+
+
+def test_small_batch_path_ties_and_shared_experts():
+    """Logits drawn from a handful of values, so every token has ties (to the
+    lower expert id) and several tokens pick the same experts."""
+    _torch()
+    d, ffn, E, k, T = 512, 192, 24, 6, 4
+    hl = random_layer(3300, d, ffn, E, 4, "f16", 384)
+    r = synth.rng(3301)
+    x = _x(r, T, d, "bf16")
+    lg = np.round(synth.normal_f32(r, (T, E)) * 2.0).astype(np.float32) / 2.0
+    lg[1] = lg[0]  # two tokens with identical routing
+    _check_layer(hl, x, lg, k, True, "bf16")
+
+
 # Routing and grouping of batches around 64 tokens, up to 16 selections per
 # token, 512 experts, every expert selected, and one selection per token.
 @pytest.mark.parametrize("T,E,k", [(64, 256, 16), (65, 256, 16), (64, 512, 8), (2, 3, 3),
