@@ -214,9 +214,9 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
       return rc;
     if (launched) return SMOE_OK;
   }
-  if (T >= 2 && cfg.is_default()) {
-    // a few tokens: routing, grouping and gate/up in one launch, then the
-    // grouped down stage and the combine
+  if (cfg.is_default()) {
+    // a few tokens (or one token with a shared expert): routing, grouping
+    // and gate/up in one launch, then the grouped down stage and the combine
     bool launched = false;
     if ((rc = check_hip(small_try(L, x, xmode != X_BF16, xmode == X_F32_RMS, eps, logits, T, k,
                                   norm, nsh, uids, uw, ids, w, meta, active, offs, pair_token,

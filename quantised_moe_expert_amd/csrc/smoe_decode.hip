@@ -175,7 +175,7 @@ hipError_t small_try(const LayerInfo& L, const void* x, bool xf32, bool rms, flo
   *launched = false;
   const ExpertPlan& P = L.plan;
   const int E = (int)L.desc.num_experts, bits = (int)L.desc.bits;
-  if (T < 2 || T > SB_TMAX || (int64_t)T * E > SB_KEYS) return hipSuccess;
+  if (T < 1 || T > SB_TMAX || (int64_t)T * E > SB_KEYS) return hipSuccess;
   if (L.desc.shared_ffn_dim && nsh <= 0) return hipSuccess;
   // a unit's results (tokens x rows per wave load) are staged in 64 floats
   if (T * (64 >> P.gate.lpr_log2) > 64) return hipSuccess;

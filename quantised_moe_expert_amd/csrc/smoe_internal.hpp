@@ -131,7 +131,7 @@ hipError_t decode1_try(const LayerInfo& L, const void* x, bool xf32, bool rms, f
                        int32_t* uids, float* uw, float* h, int32_t* ws_ids, float* ws_w,
                        hipStream_t stream, bool* launched);
 
-// Small batches (2..16 tokens): routing, grouping and the gate/up stage in one
+// Small batches (1..4 tokens): routing, grouping and the gate/up stage in one
 // launch, writing ids, w, meta, active, offs, pair_token, pair_of and h in the
 // grouped layout the down stage and the combine read; nsh as for the grouped
 // stages (the shared expert's parts after the routed pairs). Sets *launched =
