@@ -224,6 +224,11 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
                         "small-batch gate/up launch")))
       return rc;
     if (launched) {
+      if ((rc = check_hip(small_down_try(L, h, T, k, nsh, meta, active, offs, pair_token,
+                                         pair_of, w, out, accumulate, s, &launched),
+                          "small-batch down launch")))
+        return rc;
+      if (launched) return SMOE_OK;
       float* ysh = nsh ? y + (size_t)T * k * L.desc.d_model : nullptr;
       {
         TracedLaunch t(SMOE_KERNEL_DOWN);

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "smoe_decode_args.hpp"
+#include "smoe_small_args.hpp"
 #include "smoe_internal.hpp"
 #include "smoe_launch.hpp"
 
@@ -81,6 +82,31 @@ bool find_sb_any(int bits, int sdt, int vg, bool xf32, SbLaunch* L) {
   return find_sb<2, _Float16>(vg, xf32, L);
 }
 
+typedef hipError_t (*SdLaunch)(const SmallDownArgs&, int, hipStream_t);
+
+template <int BITS, typename ST>
+bool find_sd(int vd, SdLaunch* L) {
+#define SMOE_FIND_SD(v)               \
+  if (vd == v) {                      \
+    *L = launch_sb_down<BITS, ST, v>; \
+    return true;                      \
+  }
+  if constexpr (BITS == 4) {
+    SMOE_DEC_Q4_VD(SMOE_FIND_SD)
+  } else {
+    SMOE_DEC_Q2_VD(SMOE_FIND_SD)
+  }
+#undef SMOE_FIND_SD
+  return false;
+}
+
+bool find_sd_any(int bits, int sdt, int vd, SdLaunch* L) {
+  if (bits == 4 && sdt == SMOE_SCALE_F32) return find_sd<4, float>(vd, L);
+  if (bits == 4) return find_sd<4, _Float16>(vd, L);
+  if (sdt == SMOE_SCALE_F32) return find_sd<2, float>(vd, L);
+  return find_sd<2, _Float16>(vd, L);
+}
+
 uint64_t align16(uint64_t v) { return (v + 15) / 16 * 16; }
 
 // static LDS of k_sb_gate_up: expert masks, slots, active list, offsets,
@@ -88,6 +114,10 @@ uint64_t align16(uint64_t v) { return (v + 15) / 16 * 16; }
 constexpr uint64_t SB_STATIC_LDS = (4ull * SMOE_MAX_EXPERTS + 1) * 4 +
                                    2ull * SB_TSLOTS * SMOE_MAX_TOP_K * 4 + 64 +
                                    (DEC_THREADS / 64) * 64 * 4;
+
+// static LDS of k_sb_down: accumulators, pair scales and tokens, slots
+constexpr uint64_t SD_STATIC_LDS = (uint64_t)DEC_THREADS / 64 * SB_TSLOTS * SB_DOWN_RB * 4 +
+                                   2ull * SB_PAIRS * 4 + (2ull * SMOE_MAX_EXPERTS + 17) * 4;
 
 }  // namespace
 
@@ -234,6 +264,71 @@ hipError_t small_try(const LayerInfo& L, const void* x, bool xf32, bool rms, flo
   {
     TracedLaunch t(SMOE_KERNEL_GATE_UP);
     e = sb(A, nwg, stream);
+  }
+  if (e != hipSuccess) return e;
+  *launched = true;
+  return hipSuccess;
+}
+
+hipError_t small_down_try(const LayerInfo& L, const float* h, int T, int k, int nsh,
+                          const int* meta, const int* active, const int* offs,
+                          const int* pair_token, const int* pair_of, const float* w, float* out,
+                          int accumulate, hipStream_t stream, bool* launched) {
+  *launched = false;
+  const ExpertPlan& P = L.plan;
+  const int bits = (int)L.desc.bits;
+  if (T < 1 || T > SB_TSLOTS || k > SMOE_MAX_TOP_K || nsh < 0 || nsh > 16) return hipSuccess;
+  if (L.desc.shared_ffn_dim && nsh <= 0) return hipSuccess;
+  // the down rows go to at most 16 lanes each, as in the one-token down stage
+  const int lg_d = P.down.lpr_log2 < 4 ? P.down.lpr_log2 : 4;
+  const int vd = P.down.words_per_row >> lg_d;
+  SdLaunch sd;
+  if (!find_sd_any(bits, (int)L.desc.scale_dtype, vd, &sd)) return hipSuccess;
+  const int rpwd = 64 >> lg_d;
+  int rb = (P.d_model + DEC_NWG - 1) / DEC_NWG;
+  rb = (rb + rpwd - 1) / rpwd * rpwd;
+  rb = rb < sb_down_loads(vd) * rpwd ? rb : sb_down_loads(vd) * rpwd;
+  if (rb > SB_DOWN_RB) return hipSuccess;
+  // one pair's h as fp16 pairs in the wave's LDS region
+  if ((int64_t)P.ffn * bits / 32 > 64 * (DEC_HC / (bits == 2 ? 2 : 1))) return hipSuccess;
+  SmallDownArgs A{};
+  A.blobs = L.blobs;
+  A.stride = L.desc.blob_stride;
+  A.table = L.table;
+  A.dc = P.down.codes_off;
+  A.ds = P.down.scales_off;
+  if (nsh) {
+    A.shared = L.shared;
+    A.sdc = L.shared_plan.down.codes_off;
+    A.sds = L.shared_plan.down.scales_off;
+  }
+  A.d = P.d_model;
+  A.ffn = P.ffn;
+  A.k = k;
+  A.T = T;
+  A.nsh = nsh;
+  A.lg_d = lg_d;
+  A.rb = rb;
+  A.h = h;
+  A.meta = meta;
+  A.active = active;
+  A.offs = offs;
+  A.pair_token = pair_token;
+  A.pair_of = pair_of;
+  A.w = w;
+  A.out = out;
+  A.accumulate = accumulate;
+  // dynamic LDS: every pair's h as fp16 pairs and their offsets
+  const uint64_t np = (uint64_t)T * k + (uint64_t)nsh * T;
+  const uint64_t wd = (uint64_t)P.ffn * bits / 32;
+  A.lds_hk = (int)align16(np * wd * (16 / bits) * 4);
+  A.lds_total = (int)align16(A.lds_hk + np * wd * 4);
+  if (A.lds_total + SD_STATIC_LDS > 150 * 1024) return hipSuccess;
+  const int nwg = (P.d_model + rb - 1) / rb;
+  hipError_t e;
+  {
+    TracedLaunch t(SMOE_KERNEL_DOWN);
+    e = sd(A, nwg, stream);
   }
   if (e != hipSuccess) return e;
   *launched = true;

@@ -58,45 +58,6 @@ hipError_t launch_dec_gate_up(const DecodeArgs& A, int nwg, hipStream_t s);
 template <int BITS, typename ST, int VD>
 hipError_t launch_dec_down(const DecodeArgs& A, int nwg, hipStream_t s);
 
-// Small batches (2..4 tokens): routing, grouping and the gate/up stage in
-// one launch (smoe_small.hpp). Its vector dot products cost about 300
-// instructions per token and row pair, three times what the grouped
-// matrix-core stage spends, so past four tokens the grouped stages win.
-constexpr int SB_TMAX = 4;       // tokens per call on this path
-constexpr int SB_TSLOTS = 16;    // token slots of the kernel's LDS tables
-constexpr int SB_KEYS = 4096;    // routing keys (tokens x experts) held in LDS, max
-
-struct SmallArgs {
-  const uint8_t* blobs;  // routed bank, expert e at blobs + e * stride
-  uint64_t stride;
-  const uint64_t* table; // optional [E] blob addresses
-  const uint8_t* shared; // shared expert blob (nsh > 0)
-  uint64_t gc, gs, uc, us;       // routed gate / up codes and scales offsets
-  uint64_t sgc, sgs, suc, sus;   // the shared expert's
-  int d, ffn, E, k, T, norm, nsh;
-  int lg_g;              // log2 lanes per gate/up row
-  const void* x;         // [T, d] bf16 or fp32
-  int rms;               // apply unit-gain RMSNorm to each token
-  float eps;
-  const float* logits;   // [T, E]
-  float* h;              // [T * k + nsh * T, ffn] per grouped pair
-  // the grouped layout (read by the grouped down stage and the combine)
-  int32_t* ids;          // [T * k] selected experts
-  float* w;              // [T * k] their weights
-  int* meta;             // [0] active experts, [1] routed pairs
-  int* active;           // [E] expert of each active slot
-  int* offs;             // [active + nsh + 1] first grouped pair of each slot
-  int* pair_token;       // [T * k + nsh * T] token of each grouped pair
-  int* pair_of;          // [T * k] grouped position of pair (t, j)
-  int32_t* user_ids;     // optional [T * k]
-  float* user_w;         // optional [T * k]
-  // dynamic LDS layout (bytes)
-  int lds_lv, lds_xp, lds_k, lds_os, lds_total;
-};
-
-template <int BITS, typename ST, int VG, bool XF32>
-hipError_t launch_sb_gate_up(const SmallArgs& A, int nwg, hipStream_t s);
-
 // gate/up and down words-per-lane values with an instantiation
 #define SMOE_DEC_Q4_VG(X) X(8) X(4) X(1)
 #define SMOE_DEC_Q4_VD(X) X(12) X(11) X(8) X(6) X(4) X(2) X(1) X(16)

@@ -21,7 +21,9 @@ namespace smoe {
       const SmallArgs&, int, hipStream_t);
 #define SMOE_DEC_INST_D(vd)                                                                  \
   template hipError_t launch_dec_down<SMOE_INST_BITS, SMOE_INST_ST, vd>(const DecodeArgs&,  \
-                                                                         int, hipStream_t);
+                                                                         int, hipStream_t); \
+  template hipError_t launch_sb_down<SMOE_INST_BITS, SMOE_INST_ST, vd>(const SmallDownArgs&, \
+                                                                        int, hipStream_t);
 
 #if SMOE_INST_BITS == 4
 SMOE_DEC_Q4_VG(SMOE_DEC_INST_G)

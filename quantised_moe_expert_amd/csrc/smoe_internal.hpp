@@ -142,6 +142,15 @@ hipError_t small_try(const LayerInfo& L, const void* x, bool xf32, bool rms, flo
                      int* pair_token, int* pair_of, float* h, hipStream_t stream,
                      bool* launched);
 
+// Small batches (1..16 tokens) in the grouped layout: the down stage of every
+// grouped pair and the weighted combine (out = or += sum_j w[t, j] y[pair] +
+// the shared expert's parts) in one launch. Sets *launched = false, enqueuing
+// nothing, when the layer's shape has no instantiation.
+hipError_t small_down_try(const LayerInfo& L, const float* h, int T, int k, int nsh,
+                          const int* meta, const int* active, const int* offs,
+                          const int* pair_token, const int* pair_of, const float* w, float* out,
+                          int accumulate, hipStream_t stream, bool* launched);
+
 // y_shared (nullable): nsh partial outputs of the shared expert, [nsh][T][d],
 // summed; shared_gate (nullable, [T] logits): the shared expert's weight is
 // sigmoid(shared_gate[t]) instead of 1.

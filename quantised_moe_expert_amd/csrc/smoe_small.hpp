@@ -1,5 +1,7 @@
-// Small batches (2..4 tokens) on gfx950: routing, grouping and the gate/up
-// stage in one launch, the one-token design extended to a few tokens.
+// Small batches on gfx950, the one-token design extended to a few tokens:
+// routing, grouping and the gate/up stage in one launch (2..4 tokens, or one
+// token with a shared expert), and the down stage with the combine in one
+// launch (up to 16 tokens).
 //
 // Every workgroup routes all T tokens itself ("CMF v2 Format Specification",
 // 2.2 MoE: top-k of the logits, equal logits to the lower expert id,
@@ -18,6 +20,7 @@
 #pragma once
 
 #include "smoe_decode.hpp"
+#include "smoe_small_args.hpp"
 
 namespace smoe {
 
@@ -418,6 +421,249 @@ template <int BITS, typename ST, int VG, bool XF32>
 hipError_t launch_sb_gate_up(const SmallArgs& A, int nwg, hipStream_t s) {
   if (!sb_narrow<BITS, VG, XF32>()) nwg = DEC_NWG;
   auto kernel = k_sb_gate_up<BITS, ST, VG, XF32>;
+  if (A.lds_total > 65536) {  // workgroups of more than 64 KB of LDS need the limit raised
+    const hipError_t e = hipFuncSetAttribute(
+        (const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, A.lds_total);
+    if (e != hipSuccess) return e;
+  }
+  return launch_kernel_lds(kernel, dim3(nwg), dim3(DEC_THREADS), (unsigned)A.lds_total, s, A);
+}
+
+
+// k_sb_down: the down projection of every grouped pair and the weighted
+// combine of a small batch in one launch. Workgroup w owns output rows
+// [w rb, (w + 1) rb) of every token. Its waves first turn the h of every
+// grouped pair into fp16 pairs scaled by a power of two (as the one-token
+// down stage does, one pair per wave at a time), all of them held in LDS.
+// Wave j then takes the units j, j + 8, ... (the shared expert's parts, then
+// the active experts), a unit's rows (16 lanes per row, four rows per wave
+// load) in batches of two loads with the next batch requested before the
+// current one is computed, and adds weight x row into its per-token
+// accumulators for each pair of the unit. The accumulators of the eight waves
+// are added in wave order and written (or added to the residual stream).
+template <int BITS, typename ST, int VD>
+__global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_sb_down(SmallDownArgs A) {
+  constexpr int PPW = QT<BITS>::PPW;
+  constexpr int WPW = QT<BITS>::WPW;
+  constexpr int NPOS = QT<BITS>::NPOS;
+  using SPD = ScalePlan<BITS, VD>;
+  constexpr int UB = VD > 12 ? 1 : 2;  // row loads per lane per batch
+  constexpr int N4 = LaneMap<VD>::N4, RT = LaneMap<VD>::R;
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ float s_acc[DEC_WAVES][SB_TSLOTS * SB_DOWN_RB];
+  __shared__ float s_os[SB_PAIRS];             // weight / (M S) of each grouped pair
+  __shared__ int s_pt[SB_PAIRS];               // token of each grouped pair
+  __shared__ int s_act[SMOE_MAX_EXPERTS];      // expert of each active slot
+  __shared__ int s_off[SMOE_MAX_EXPERTS + 17]; // first pair of each slot
+  uint32_t* s_hp = (uint32_t*)smem;            // [pairs][Wd * PPW] fp16 pairs in lane-map order
+  float* s_hk = (float*)(smem + A.lds_hk);     // [pairs][Wd] their offsets
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = A.T, nsh = A.nsh, P = T * A.k, NP = P + nsh * T;
+  const int nact = A.meta[0], nq = nsh + nact;
+  // 1. the grouped layout and the pair weights (the shared expert's parts: 1)
+  for (int i = tid; i < nact; i += DEC_THREADS) s_act[i] = A.active[i];
+  for (int i = tid; i <= nact + nsh; i += DEC_THREADS) s_off[i] = A.offs[i];
+  for (int i = tid; i < NP; i += DEC_THREADS) s_pt[i] = A.pair_token[i];
+  for (int i = tid; i < P; i += DEC_THREADS) s_os[A.pair_of[i]] = A.w[i];
+  for (int i = tid; i < nsh * T; i += DEC_THREADS) s_os[P + i] = 1.0f;
+  for (int i = lane; i < SB_TSLOTS * SB_DOWN_RB; i += 64) s_acc[wave][i] = 0.f;
+  __syncthreads();
+
+  const int lgd = A.lg_d, LPRD = 1 << lgd, lrd = lane & (LPRD - 1), rsd = lane >> lgd;
+  const int RPWD = 64 >> lgd;
+  const int r0 = (int)blockIdx.x * A.rb;
+  int nrows = A.d - r0;
+  nrows = nrows < 0 ? 0 : (nrows > A.rb ? A.rb : nrows);
+  const int upx = (nrows + RPWD - 1) / RPWD;  // row loads per unit, 1..sb_down_loads(VD)
+  // this wave's batches: its units wave, wave + 8, ..., each in nb batches
+  const int nb = (upx + UB - 1) / UB;
+  const int nbt = (wave < nq ? (nq - wave + DEC_WAVES - 1) / DEC_WAVES : 0) * nb;
+  const int Wd = A.ffn * BITS / 32, Gd = A.ffn / 64, HPS = Wd * PPW;
+  int sgd[SPD::NS], tmd;
+  scale_groups<BITS, VD>(lrd, LPRD, sgd, tmd);
+
+  struct DB {
+    uint32_t w[UB][VD];
+    float s[UB][SPD::NS];
+  };
+  // the rows of batch b of the wave (a wave past its last batch requests the
+  // last one again, so that the number of loads in flight is the same on
+  // every path and the waits count them exactly)
+  auto issue = [&](DB& D, int b) {
+    b = b < nbt ? b : (nbt > 0 ? nbt - 1 : 0);
+    int q = wave + (b / nb) * DEC_WAVES;
+    const int i0 = (b % nb) * UB;
+    q = q < nq ? q : nq - 1;
+    const uint32_t* cbase;
+    const ST* sbase;
+    int cpitch, spitch;
+    if (q < nsh) {  // part q of the shared expert: columns [q ffn, (q + 1) ffn)
+      cbase = (const uint32_t*)(A.shared + A.sdc) + (size_t)q * Wd;
+      sbase = (const ST*)(A.shared + A.sds) + (size_t)q * Gd;
+      cpitch = nsh * Wd;
+      spitch = nsh * Gd;
+    } else {
+      const uint8_t* blob = expert_blob(A.blobs, A.stride, A.table, s_act[q - nsh]);
+      cbase = (const uint32_t*)(blob + A.dc);
+      sbase = (const ST*)(blob + A.ds);
+      cpitch = Wd;
+      spitch = Gd;
+    }
+#pragma unroll
+    for (int i = 0; i < UB; ++i) {
+      const int ri = i0 + i < upx ? i0 + i : upx - 1;
+      int row = r0 + ri * RPWD + rsd;
+      row = row < A.d ? row : A.d - 1;
+      load_row_words<VD, true>(cbase + (size_t)row * cpitch, lrd, LPRD, D.w[i]);
+      load_row_scales<BITS, VD, ST, true>(sbase + (size_t)row * spitch, sgd, Gd, D.s[i]);
+    }
+  };
+  // batch b's rows against the pairs of its unit, into the wave's accumulators
+  auto compute = [&](const DB& D, int b) {
+    const int q = wave + (b / nb) * DEC_WAVES;
+    const int i0 = (b % nb) * UB;
+    const int p0 = q < nsh ? P + q * T : s_off[q - nsh];
+    const int p1 = q < nsh ? p0 + T : s_off[q - nsh + 1];
+#pragma unroll 1
+    for (int p = p0; p < p1; ++p) {
+      XRegs<BITS, VD, false> H;
+      const uint32_t* hp = s_hp + (size_t)p * HPS;
+#pragma unroll
+      for (int w = 0; w < VD; ++w) {
+        const uint32_t* src = hp + (w * LPRD + lrd) * PPW;
+#pragma unroll
+        for (int qq = 0; qq < PPW; qq += 4) {
+          const u32x4 v = *(const u32x4*)(src + qq);
+          // components to scalars before the bit casts (a bit cast of a
+          // vector component reads the vector's first element)
+          const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+          H.hi[w][qq] = __builtin_bit_cast(f16x2, v0);
+          H.hi[w][qq + 1] = __builtin_bit_cast(f16x2, v1);
+          H.hi[w][qq + 2] = __builtin_bit_cast(f16x2, v2);
+          H.hi[w][qq + 3] = __builtin_bit_cast(f16x2, v3);
+        }
+        H.K[w] = s_hk[(size_t)p * Wd + w * LPRD + lrd];
+      }
+      fold_k(H);
+      const float os = s_os[p];
+      float* acc = s_acc[wave] + s_pt[p] * SB_DOWN_RB;
+#pragma unroll
+      for (int i = 0; i < UB; ++i) {
+        if (i0 + i < upx) {  // wave-uniform
+          float a = lane_row<BITS, VD, false>(D.w[i], H, D.s[i], tmd);
+          a = seg_sum(a, lgd);
+          const int rl = (i0 + i) * RPWD + rsd;
+          if (lrd == LPRD - 1 && rl < nrows) acc[rl] += a * os;
+        }
+      }
+    }
+  };
+
+  // 2. h of this wave's first pair, then the rows of its first unit, then
+  //    every pair of the wave into LDS, then the rows of its second unit
+  const float* h0 = A.h + (size_t)(wave < NP ? wave : NP - 1) * A.ffn;
+  float hv[DEC_HC][WPW];
+  auto load_h = [&](const float* hrow) {
+#pragma unroll
+    for (int j = 0; j < DEC_HC; ++j) {
+      const int c = lane + 64 * j;
+      const float* src = hrow + (size_t)(c < Wd ? c : Wd - 1) * WPW;
+#pragma unroll
+      for (int i = 0; i < WPW / 4; ++i) {
+        const f32x4 v = *(const f32x4*)(src + 4 * i);
+        hv[j][4 * i] = v.x;
+        hv[j][4 * i + 1] = v.y;
+        hv[j][4 * i + 2] = v.z;
+        hv[j][4 * i + 3] = v.w;
+      }
+    }
+  };
+  auto convert = [&](int p) {
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < DEC_HC; ++j)
+      if (lane + 64 * j < Wd)
+#pragma unroll
+        for (int i = 0; i < WPW; ++i) m = fmaxf(m, fabsf(hv[j][i]));
+    m = lane63(seg_max(m, 6));
+    const float S = pow2_prescale(m);
+    uint32_t* hp = s_hp + (size_t)p * HPS;
+    float* hk = s_hk + (size_t)p * Wd;
+#pragma unroll
+    for (int j = 0; j < DEC_HC; ++j) {
+      const int c = lane + 64 * j;
+      if (c < Wd) {
+        int lr, sl;
+        if (c < 4 * N4 * LPRD) {
+          const int ch = c / (4 * LPRD), rem = c - ch * 4 * LPRD;
+          lr = rem >> 2;
+          sl = 4 * ch + (rem & 3);
+        } else {
+          const int rem = c - 4 * N4 * LPRD;
+          lr = rem / (RT > 0 ? RT : 1);
+          sl = 4 * N4 + (rem - lr * (RT > 0 ? RT : 1));
+        }
+        float kk = 0.f;
+        uint32_t pw[PPW];
+#pragma unroll
+        for (int qq = 0; qq < PPW; ++qq) {
+          const int hs = qq / NPOS, pos = qq % NPOS;
+          const int ia = hs * NPOS + pos, ib = ia + WPW / 2;
+          const float f = S * (1.0f / (float)(1 << (BITS * pos)));
+          const _Float16 ha = (_Float16)(hv[j][ia] * f), hb = (_Float16)(hv[j][ib] * f);
+          pw[qq] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
+          kk = fmaf((float)ha + (float)hb, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)),
+                    kk);
+        }
+        uint32_t* dst = hp + (sl * LPRD + lr) * PPW;
+#pragma unroll
+        for (int qq = 0; qq < PPW; qq += 4)
+          *(u32x4*)(dst + qq) = u32x4{pw[qq], pw[qq + 1], pw[qq + 2], pw[qq + 3]};
+        hk[sl * LPRD + lr] = kk;
+      }
+    }
+    if (lane == 0) s_os[p] = s_os[p] / (QT<BITS>::M * S);
+  };
+  load_h(h0);
+  DB dA, dB;
+  issue(dA, 0);
+  // the first pair's h arrives before the rows requested after it
+  if (wave < NP) convert(wave);
+#pragma unroll 1
+  for (int p = wave + DEC_WAVES; p < NP; p += DEC_WAVES) {
+    load_h(A.h + (size_t)p * A.ffn);
+    convert(p);
+  }
+  issue(dB, 1);
+  __syncthreads();
+
+  // 3. the wave's batches, two in flight
+#pragma unroll 1
+  for (int b = 0; b < nbt; b += 2) {
+    compute(dA, b);
+    if (b + 1 >= nbt) break;
+    issue(dA, b + 2);
+    compute(dB, b + 1);
+    issue(dB, b + 3);
+  }
+  __syncthreads();
+  // 4. the output rows of every token: the waves' sums in wave order
+  for (int i = tid; i < T * nrows; i += DEC_THREADS) {
+    const int t = i / nrows, rl = i - t * nrows;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < DEC_WAVES; ++w) acc += s_acc[w][t * SB_DOWN_RB + rl];
+    float* dst = A.out + (size_t)t * A.d + r0 + rl;
+    *dst = A.accumulate ? *dst + acc : acc;
+  }
+}
+
+template <int BITS, typename ST, int VD>
+hipError_t launch_sb_down(const SmallDownArgs& A, int nwg, hipStream_t s) {
+  auto kernel = k_sb_down<BITS, ST, VD>;
   if (A.lds_total > 65536) {  // workgroups of more than 64 KB of LDS need the limit raised
     const hipError_t e = hipFuncSetAttribute(
         (const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, A.lds_total);

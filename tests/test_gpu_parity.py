@@ -142,6 +142,12 @@ SMALL_BATCH = [
     (512, 320, 16, 16, 2, 2, "f32", True, 640),
     (2048, 1408, 64, 6, 4, 4, "f32", False, 2816),
     (768, 192, 40, 7, 4, 2, "f16", False, 0),
+    # one token with a shared expert; a row count that leaves the last
+    # workgroup of the down stage a partial block (12 rows per workgroup);
+    # pairs whose h exceeds the down stage's LDS (grouped down and combine)
+    (2048, 1408, 64, 6, 1, 4, "f16", False, 2816),
+    (2560, 512, 32, 6, 3, 4, "f32", True, 1024),
+    (1024, 1536, 64, 16, 4, 4, "f16", True, 0),
 ]
 
 
@@ -315,12 +321,12 @@ def test_single_token_workspace_reuse():
         assert rel_l2(out.cpu().numpy(), ref[i % 4]) <= TOL, i
 
 
-def test_decode_step_multi_token_small():
+@pytest.mark.parametrize("T,shared", [(3, 0), (2, 640)])
+def test_decode_step_multi_token_small(T, shared):
     torch = _torch()
     import quantised_moe_expert_amd as smoe
-    hls = [random_layer(40 + l, 512, 320, 16, 4, "f16") for l in range(3)]
-    r = synth.rng(41)
-    T = 3
+    hls = [random_layer(40 + l + shared, 512, 320, 16, 4, "f16", shared) for l in range(3)]
+    r = synth.rng(41 + T)
     x = synth.normal_f32(r, (T, 512))
     lg = synth.normal_f32(r, (3, T, 16))
     dls = [DeviceLayer(h) for h in hls]
