@@ -282,6 +282,15 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
                    "gate/up launch");
   }
   if (rc) return rc;
+  if (cfg.is_default() && !side_lock.owns_lock() && !gmk_wanted(pairs, max_slots)) {
+    // up to 16 tokens: the down stage and the combine in one launch
+    bool launched = false;
+    if ((rc = check_hip(small_down_try(L, h, T, k, nsh, meta, active, offs, pair_token, pair_of,
+                                       w, out, accumulate, s, &launched),
+                        "small-batch down launch")))
+      return rc;
+    if (launched) return SMOE_OK;
+  }
   {
     TracedLaunch t(SMOE_KERNEL_DOWN);
     rc = check_hip(launch_down(L, false, h, T, pairs, max_slots, meta, active, offs, y, s, prep,

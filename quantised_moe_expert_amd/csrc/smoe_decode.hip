@@ -117,7 +117,7 @@ constexpr uint64_t SB_STATIC_LDS = (4ull * SMOE_MAX_EXPERTS + 1) * 4 +
 
 // static LDS of k_sb_down: accumulators, pair scales and tokens, slots
 constexpr uint64_t SD_STATIC_LDS = (uint64_t)DEC_THREADS / 64 * SB_TSLOTS * SB_DOWN_RB * 4 +
-                                   2ull * SB_PAIRS * 4 + (2ull * SMOE_MAX_EXPERTS + 17) * 4;
+                                   2ull * SB_PAIRS * 4 + (SMOE_MAX_EXPERTS + 2ull * DEC_THREADS) * 4;
 
 }  // namespace
 
@@ -318,12 +318,14 @@ hipError_t small_down_try(const LayerInfo& L, const float* h, int T, int k, int 
   A.w = w;
   A.out = out;
   A.accumulate = accumulate;
-  // dynamic LDS: every pair's h as fp16 pairs and their offsets
+  // dynamic LDS: every pair's h as fp16 pairs, and their offsets
   const uint64_t np = (uint64_t)T * k + (uint64_t)nsh * T;
+  if (np > SB_PAIRS) return hipSuccess;
   const uint64_t wd = (uint64_t)P.ffn * bits / 32;
   A.lds_hk = (int)align16(np * wd * (16 / bits) * 4);
   A.lds_total = (int)align16(A.lds_hk + np * wd * 4);
   if (A.lds_total + SD_STATIC_LDS > 150 * 1024) return hipSuccess;
+  A.E = (int)L.desc.num_experts;
   const int nwg = (P.d_model + rb - 1) / rb;
   hipError_t e;
   {

@@ -432,56 +432,187 @@ hipError_t launch_sb_gate_up(const SmallArgs& A, int nwg, hipStream_t s) {
 
 // k_sb_down: the down projection of every grouped pair and the weighted
 // combine of a small batch in one launch. Workgroup w owns output rows
-// [w rb, (w + 1) rb) of every token. Its waves first turn the h of every
-// grouped pair into fp16 pairs scaled by a power of two (as the one-token
-// down stage does, one pair per wave at a time), all of them held in LDS.
-// Wave j then takes the units j, j + 8, ... (the shared expert's parts, then
-// the active experts), a unit's rows (16 lanes per row, four rows per wave
-// load) in batches of two loads with the next batch requested before the
-// current one is computed, and adds weight x row into its per-token
-// accumulators for each pair of the unit. The accumulators of the eight waves
-// are added in wave order and written (or added to the residual stream).
-template <int BITS, typename ST, int VD>
+// [w rb, (w + 1) rb) of every token. Every wave first requests the grouped
+// layout and the h of its pairs (pairs j, j + 8, ... of the grouped order),
+// then the rows of its first batch; it turns its pairs' h into fp16 pairs
+// scaled by a power of two (as the one-token down stage does), all of them
+// held in LDS. The units (the active experts, then the shared expert's
+// parts: the grouped pairs in order) are split into eight contiguous ranges
+// of about equal pairs plus units, one per wave; a unit's rows (16 lanes per
+// row, four rows per wave load) go in batches of two loads with the next
+// batch requested before the current one is computed, and weight x row is
+// added into the wave's per-token accumulators for each pair of the unit.
+// The accumulators of the eight waves are added in wave order and written
+// (or added to the residual stream).
+// one thread per grouped pair and per expert when the layout is staged
+static_assert(SB_PAIRS <= DEC_THREADS && SMOE_MAX_EXPERTS <= DEC_THREADS, "k_sb_down staging");
+
+// TBL: experts addressed through A.table (host offload), a template
+// parameter so that the resident-bank kernel has no conditional load (which
+// would make every wait on an earlier load wait for the row loads too).
+template <int BITS, typename ST, int VD, bool TBL>
 __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_sb_down(SmallDownArgs A) {
   constexpr int PPW = QT<BITS>::PPW;
   constexpr int WPW = QT<BITS>::WPW;
   constexpr int NPOS = QT<BITS>::NPOS;
   using SPD = ScalePlan<BITS, VD>;
-  constexpr int UB = VD > 12 ? 1 : 2;  // row loads per lane per batch
+  constexpr int UB = VD > (BITS == 2 ? 8 : 12) ? 1 : 2;  // row loads per lane per batch
+  // pairs whose h a wave requests at once (all of a wave's pairs when there
+  // are at most 32 of them: their loads then go out before the rows')
+  constexpr int HB = 4;
+  // h code words per lane (Q2 rows of h hold at most 128 words: the LDS
+  // region of one pair)
+  constexpr int HC = BITS == 2 ? DEC_HC / 2 : DEC_HC;
   constexpr int N4 = LaneMap<VD>::N4, RT = LaneMap<VD>::R;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float s_acc[DEC_WAVES][SB_TSLOTS * SB_DOWN_RB];
-  __shared__ float s_os[SB_PAIRS];             // weight / (M S) of each grouped pair
-  __shared__ int s_pt[SB_PAIRS];               // token of each grouped pair
-  __shared__ int s_act[SMOE_MAX_EXPERTS];      // expert of each active slot
-  __shared__ int s_off[SMOE_MAX_EXPERTS + 17]; // first pair of each slot
-  uint32_t* s_hp = (uint32_t*)smem;            // [pairs][Wd * PPW] fp16 pairs in lane-map order
+  __shared__ float s_os[SB_PAIRS + 1];         // weight / (M S) of each grouped pair, a spare
+  __shared__ int s_pt[DEC_THREADS];            // token of each grouped pair
+  __shared__ int s_act[DEC_THREADS];           // expert of each active slot
+  __shared__ int s_off[2 * DEC_THREADS];       // first pair of each unit, then the pair count
+  uint32_t* s_hp = (uint32_t*)smem;            // [pairs][Wd * PPW] fp16 pairs, lane-map order
   float* s_hk = (float*)(smem + A.lds_hk);     // [pairs][Wd] their offsets
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = A.T, nsh = A.nsh, P = T * A.k, NP = P + nsh * T;
-  const int nact = A.meta[0], nq = nsh + nact;
-  // 1. the grouped layout and the pair weights (the shared expert's parts: 1)
-  for (int i = tid; i < nact; i += DEC_THREADS) s_act[i] = A.active[i];
-  for (int i = tid; i <= nact + nsh; i += DEC_THREADS) s_off[i] = A.offs[i];
-  for (int i = tid; i < NP; i += DEC_THREADS) s_pt[i] = A.pair_token[i];
-  for (int i = tid; i < P; i += DEC_THREADS) s_os[A.pair_of[i]] = A.w[i];
-  for (int i = tid; i < nsh * T; i += DEC_THREADS) s_os[P + i] = 1.0f;
+  const int Wd = A.ffn * BITS / 32, Gd = A.ffn / 64, HPS = Wd * PPW;
+  const int lgd = A.lg_d, LPRD = 1 << lgd, lrd = lane & (LPRD - 1), rsd = lane >> lgd;
+  const int RPWD = 64 >> lgd;
+  // h of HB pairs, code word c = lane + 64 j per lane (coalesced)
+  float hv[HB][HC][WPW];
+  // (a request past the wave's pairs reads one address in every lane: it
+  // keeps the count of loads in flight fixed and costs one cache line)
+  auto load_h = [&](int r, int p, bool real) {
+    const float* hrow = A.h + (size_t)p * A.ffn;
+#pragma unroll
+    for (int j = 0; j < HC; ++j) {
+      const int c = real ? lane + 64 * j : 0;
+      const float* src = hrow + (size_t)(c < Wd ? c : Wd - 1) * WPW;
+#pragma unroll
+      for (int i = 0; i < WPW / 4; ++i) {
+        const f32x4 v = *(const f32x4*)(src + 4 * i);
+        hv[r][j][4 * i] = v.x;
+        hv[r][j][4 * i + 1] = v.y;
+        hv[r][j][4 * i + 2] = v.z;
+        hv[r][j][4 * i + 3] = v.w;
+      }
+    }
+  };
+  // pair p's h (in hv[r]) as fp16 pairs under a power of two, with the
+  // offsets, at the lane-map slot of each code word
+  // the lane-map slot (row word w, lane lr of the row) of this lane's code
+  // words c = lane + 64 j of h, -1 past the row
+  int hslot[HC];
+#pragma unroll
+  for (int j = 0; j < HC; ++j) {
+    const int c = lane + 64 * j;
+    int lr, sl;
+    if (c < 4 * N4 * LPRD) {
+      const int ch = c / (4 * LPRD), rem = c - ch * 4 * LPRD;
+      lr = rem >> 2;
+      sl = 4 * ch + (rem & 3);
+    } else {
+      const int rem = c - 4 * N4 * LPRD;
+      lr = rem / (RT > 0 ? RT : 1);
+      sl = 4 * N4 + (rem - lr * (RT > 0 ? RT : 1));
+    }
+    hslot[j] = c < Wd ? sl * LPRD + lr : -1;
+  }
+  auto convert = [&](int r, int p) {
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < HC; ++j)
+      if (lane + 64 * j < Wd)
+#pragma unroll
+        for (int i = 0; i < WPW; ++i) m = fmaxf(m, fabsf(hv[r][j][i]));
+    m = lane63(seg_max(m, 6));
+    const float S = pow2_prescale(m);
+    uint32_t* hp = s_hp + (size_t)p * HPS;
+    float* hk = s_hk + (size_t)p * Wd;
+#pragma unroll
+    for (int j = 0; j < HC; ++j) {
+      if (hslot[j] >= 0) {
+        float kk = 0.f;
+        uint32_t pw[PPW];
+#pragma unroll
+        for (int qq = 0; qq < PPW; ++qq) {
+          const int hs = qq / NPOS, pos = qq % NPOS;
+          const int ia = hs * NPOS + pos, ib = ia + WPW / 2;
+          const float f = S * (1.0f / (float)(1 << (BITS * pos)));
+          const _Float16 ha = (_Float16)(hv[r][j][ia] * f), hb = (_Float16)(hv[r][j][ib] * f);
+          pw[qq] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
+          kk = fmaf((float)ha + (float)hb, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)),
+                    kk);
+        }
+        uint32_t* dst = hp + hslot[j] * PPW;
+#pragma unroll
+        for (int qq = 0; qq < PPW; qq += 4)
+          *(u32x4*)(dst + qq) = u32x4{pw[qq], pw[qq + 1], pw[qq + 2], pw[qq + 3]};
+        hk[hslot[j]] = kk;
+      }
+    }
+    if (lane == 0) s_os[p] = s_os[p] / (QT<BITS>::M * S);
+  };
+
+  // this wave's pairs: wave, wave + 8, ... (requests past the last one
+  // repeat it, so that the number of loads in flight is the same on every
+  // path and the waits count them exactly)
+  const int npw = wave < NP ? (NP - wave + DEC_WAVES - 1) / DEC_WAVES : 0;
+  auto pair_of_wave = [&](int i) {
+    i = i < npw ? i : npw - 1;
+    return i >= 0 ? wave + i * DEC_WAVES : 0;
+  };
+  // 1. the grouped layout (loads clamped to the buffers' sizes), then the h
+  //    of the wave's first HB pairs; the layout goes to LDS once it arrives
+  const int nact = A.meta[0], nq = nact + nsh;
+  const int a_act = A.active[tid < A.E ? tid : A.E - 1];
+  const int a_off0 = A.offs[tid <= A.E + nsh ? tid : A.E + nsh];
+  const int a_off1 = A.offs[tid + DEC_THREADS <= A.E + nsh ? tid + DEC_THREADS : A.E + nsh];
+  const int a_pt = A.pair_token[tid < NP ? tid : NP - 1];
+  const int a_po = A.pair_of[tid < P ? tid : P - 1];
+  const float a_w = A.w[tid < P ? tid : P - 1];
+  if (npw <= 1) {  // wave-uniform: one pair (or none) takes one pair's loads
+    load_h(0, pair_of_wave(0), true);
+  } else {
+#pragma unroll
+    for (int r = 0; r < HB; ++r) load_h(r, pair_of_wave(r), r < npw);
+  }
+  // stores without conditions, so that the compiler keeps every load before
+  // the h loads (a load moved under a condition would be waited for with
+  // all the loads in flight); entries past the layout's are never read
+  s_act[tid] = a_act;
+  s_off[tid] = a_off0;
+  s_off[tid + DEC_THREADS] = a_off1;
+  s_pt[tid] = a_pt;
+  // pair weights at the grouped position, the shared expert's parts 1
+  s_os[tid < P ? a_po : (tid < NP ? tid : SB_PAIRS)] = tid < P ? a_w : 1.0f;
   for (int i = lane; i < SB_TSLOTS * SB_DOWN_RB; i += 64) s_acc[wave][i] = 0.f;
   __syncthreads();
 
-  const int lgd = A.lg_d, LPRD = 1 << lgd, lrd = lane & (LPRD - 1), rsd = lane >> lgd;
-  const int RPWD = 64 >> lgd;
+
   const int r0 = (int)blockIdx.x * A.rb;
   int nrows = A.d - r0;
   nrows = nrows < 0 ? 0 : (nrows > A.rb ? A.rb : nrows);
   const int upx = (nrows + RPWD - 1) / RPWD;  // row loads per unit, 1..sb_down_loads(VD)
-  // this wave's batches: its units wave, wave + 8, ..., each in nb batches
-  const int nb = (upx + UB - 1) / UB;
-  const int nbt = (wave < nq ? (nq - wave + DEC_WAVES - 1) / DEC_WAVES : 0) * nb;
-  const int Wd = A.ffn * BITS / 32, Gd = A.ffn / 64, HPS = Wd * PPW;
+  const int nb = (upx + UB - 1) / UB;         // batches per unit
+  // this wave's units: a contiguous range, the units split so that each wave
+  // gets about the same count of pairs plus units (unit u starts at
+  // s_off[u] + u of NP + nq; wave w takes the units starting in
+  // [w (NP + nq) / 8, (w + 1) (NP + nq) / 8))
+  const int cost = NP + nq;
+  auto first_unit = [&](int w) {  // the first unit whose start is >= w cost / 8
+    int lo = 0, hi = nq;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((s_off[mid] + mid) * DEC_WAVES >= w * cost) hi = mid;
+      else lo = mid + 1;
+    }
+    return lo;
+  };
+  const int u0 = first_unit(wave), u1 = first_unit(wave + 1);
+  const int nbt = (u1 - u0) * nb;  // this wave's batches, nb per unit
   int sgd[SPD::NS], tmd;
   scale_groups<BITS, VD>(lrd, LPRD, sgd, tmd);
 
@@ -494,19 +625,20 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_sb_down(Small
   // every path and the waits count them exactly)
   auto issue = [&](DB& D, int b) {
     b = b < nbt ? b : (nbt > 0 ? nbt - 1 : 0);
-    int q = wave + (b / nb) * DEC_WAVES;
+    int q = u0 + b / nb;
     const int i0 = (b % nb) * UB;
     q = q < nq ? q : nq - 1;
     const uint32_t* cbase;
     const ST* sbase;
     int cpitch, spitch;
-    if (q < nsh) {  // part q of the shared expert: columns [q ffn, (q + 1) ffn)
-      cbase = (const uint32_t*)(A.shared + A.sdc) + (size_t)q * Wd;
-      sbase = (const ST*)(A.shared + A.sds) + (size_t)q * Gd;
+    if (q >= nact) {  // part v of the shared expert: columns [v ffn, (v + 1) ffn)
+      const int v = q - nact;
+      cbase = (const uint32_t*)(A.shared + A.sdc) + (size_t)v * Wd;
+      sbase = (const ST*)(A.shared + A.sds) + (size_t)v * Gd;
       cpitch = nsh * Wd;
       spitch = nsh * Gd;
     } else {
-      const uint8_t* blob = expert_blob(A.blobs, A.stride, A.table, s_act[q - nsh]);
+      const uint8_t* blob = expert_blob(A.blobs, A.stride, TBL ? A.table : nullptr, s_act[q]);
       cbase = (const uint32_t*)(blob + A.dc);
       sbase = (const ST*)(blob + A.ds);
       cpitch = Wd;
@@ -523,10 +655,9 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_sb_down(Small
   };
   // batch b's rows against the pairs of its unit, into the wave's accumulators
   auto compute = [&](const DB& D, int b) {
-    const int q = wave + (b / nb) * DEC_WAVES;
+    const int q = u0 + b / nb;
     const int i0 = (b % nb) * UB;
-    const int p0 = q < nsh ? P + q * T : s_off[q - nsh];
-    const int p1 = q < nsh ? p0 + T : s_off[q - nsh + 1];
+    const int p0 = s_off[q], p1 = s_off[q + 1];
 #pragma unroll 1
     for (int p = p0; p < p1; ++p) {
       XRegs<BITS, VD, false> H;
@@ -562,80 +693,20 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_sb_down(Small
     }
   };
 
-  // 2. h of this wave's first pair, then the rows of its first unit, then
-  //    every pair of the wave into LDS, then the rows of its second unit
-  const float* h0 = A.h + (size_t)(wave < NP ? wave : NP - 1) * A.ffn;
-  float hv[DEC_HC][WPW];
-  auto load_h = [&](const float* hrow) {
-#pragma unroll
-    for (int j = 0; j < DEC_HC; ++j) {
-      const int c = lane + 64 * j;
-      const float* src = hrow + (size_t)(c < Wd ? c : Wd - 1) * WPW;
-#pragma unroll
-      for (int i = 0; i < WPW / 4; ++i) {
-        const f32x4 v = *(const f32x4*)(src + 4 * i);
-        hv[j][4 * i] = v.x;
-        hv[j][4 * i + 1] = v.y;
-        hv[j][4 * i + 2] = v.z;
-        hv[j][4 * i + 3] = v.w;
-      }
-    }
-  };
-  auto convert = [&](int p) {
-    float m = 0.f;
-#pragma unroll
-    for (int j = 0; j < DEC_HC; ++j)
-      if (lane + 64 * j < Wd)
-#pragma unroll
-        for (int i = 0; i < WPW; ++i) m = fmaxf(m, fabsf(hv[j][i]));
-    m = lane63(seg_max(m, 6));
-    const float S = pow2_prescale(m);
-    uint32_t* hp = s_hp + (size_t)p * HPS;
-    float* hk = s_hk + (size_t)p * Wd;
-#pragma unroll
-    for (int j = 0; j < DEC_HC; ++j) {
-      const int c = lane + 64 * j;
-      if (c < Wd) {
-        int lr, sl;
-        if (c < 4 * N4 * LPRD) {
-          const int ch = c / (4 * LPRD), rem = c - ch * 4 * LPRD;
-          lr = rem >> 2;
-          sl = 4 * ch + (rem & 3);
-        } else {
-          const int rem = c - 4 * N4 * LPRD;
-          lr = rem / (RT > 0 ? RT : 1);
-          sl = 4 * N4 + (rem - lr * (RT > 0 ? RT : 1));
-        }
-        float kk = 0.f;
-        uint32_t pw[PPW];
-#pragma unroll
-        for (int qq = 0; qq < PPW; ++qq) {
-          const int hs = qq / NPOS, pos = qq % NPOS;
-          const int ia = hs * NPOS + pos, ib = ia + WPW / 2;
-          const float f = S * (1.0f / (float)(1 << (BITS * pos)));
-          const _Float16 ha = (_Float16)(hv[j][ia] * f), hb = (_Float16)(hv[j][ib] * f);
-          pw[qq] = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
-          kk = fmaf((float)ha + (float)hb, 1024.0f + QT<BITS>::M * (float)(1 << (BITS * pos)),
-                    kk);
-        }
-        uint32_t* dst = hp + (sl * LPRD + lr) * PPW;
-#pragma unroll
-        for (int qq = 0; qq < PPW; qq += 4)
-          *(u32x4*)(dst + qq) = u32x4{pw[qq], pw[qq + 1], pw[qq + 2], pw[qq + 3]};
-        hk[sl * LPRD + lr] = kk;
-      }
-    }
-    if (lane == 0) s_os[p] = s_os[p] / (QT<BITS>::M * S);
-  };
-  load_h(h0);
+  // 2. the rows of the wave's first batch, its pairs into LDS, then the rows
+  //    of its second batch
   DB dA, dB;
   issue(dA, 0);
-  // the first pair's h arrives before the rows requested after it
-  if (wave < NP) convert(wave);
+#pragma unroll
+  for (int r = 0; r < HB; ++r)
+    if (r < npw) convert(r, pair_of_wave(r));
 #pragma unroll 1
-  for (int p = wave + DEC_WAVES; p < NP; p += DEC_WAVES) {
-    load_h(A.h + (size_t)p * A.ffn);
-    convert(p);
+  for (int i = HB; i < npw; i += HB) {
+#pragma unroll
+    for (int r = 0; r < HB; ++r) load_h(r, pair_of_wave(i + r), i + r < npw);
+#pragma unroll
+    for (int r = 0; r < HB; ++r)
+      if (i + r < npw) convert(r, pair_of_wave(i + r));
   }
   issue(dB, 1);
   __syncthreads();
@@ -663,7 +734,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES_PER_EU) void k_sb_down(Small
 
 template <int BITS, typename ST, int VD>
 hipError_t launch_sb_down(const SmallDownArgs& A, int nwg, hipStream_t s) {
-  auto kernel = k_sb_down<BITS, ST, VD>;
+  auto kernel = A.table ? k_sb_down<BITS, ST, VD, true> : k_sb_down<BITS, ST, VD, false>;
   if (A.lds_total > 65536) {  // workgroups of more than 64 KB of LDS need the limit raised
     const hipError_t e = hipFuncSetAttribute(
         (const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, A.lds_total);

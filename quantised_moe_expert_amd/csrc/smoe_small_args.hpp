@@ -67,6 +67,7 @@ struct SmallDownArgs {
   const float* w;        // [T * k] weights of the pairs (t, j)
   float* out;            // [T, d]
   int accumulate;        // out += layer(x)
+  int E;                 // routed experts (size of active; offs holds E + nsh + 1)
   int lds_hk, lds_total; // dynamic LDS: fp16 pairs of every pair's h, then their offsets
 };
 constexpr int SB_DOWN_RB = 16;  // output rows per workgroup, max

@@ -165,6 +165,32 @@ def test_small_batch_path(case, x_dtype):
     _check_layer(hl, x, lg, k, norm, x_dtype)
 
 
+# Five to sixteen tokens: the grouped routing and gate/up stages, then the
+# down stage and the combine in one launch, the pairs' h staged in LDS in
+# chunks of whole experts (several chunks for all but the smallest rows).
+SMALL_DOWN = [
+    # d, ffn, E, k, T, bits, scales, norm, shared
+    (4096, 1536, 128, 8, 8, 4, "f32", True, 0),
+    (1024, 1536, 64, 16, 12, 4, "f16", True, 0),
+    (2048, 1408, 64, 6, 16, 4, "f32", False, 2816),
+    (768, 192, 40, 7, 16, 2, "f16", False, 0),
+    (2560, 512, 32, 6, 9, 2, "f32", True, 1024),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_DOWN,
+                         ids=[f"d{c[0]}_f{c[1]}_E{c[2]}_k{c[3]}_T{c[4]}_q{c[5]}_{c[6]}"
+                              f"_n{int(c[7])}_s{c[8]}" for c in SMALL_DOWN])
+def test_small_down_path(case):
+    _torch()
+    d, ffn, E, k, T, bits, sd, norm, shared = case
+    hl = random_layer(3500 + d + E + T, d, ffn, E, bits, sd, shared)
+    r = synth.rng(3600 + T + E)
+    x = _x(r, T, d, "bf16")
+    lg = synth.normal_f32(r, (T, E))
+    _check_layer(hl, x, lg, k, norm, "bf16")
+
+
 def test_small_batch_path_ties_and_shared_experts():
     """Logits drawn from a handful of values, so every token has ties (to the
     lower expert id) and several tokens pick the same experts."""
