@@ -31,6 +31,69 @@ constexpr bool sb_narrow() {
   return !XF32 && VG * QT<BITS>::PPW <= 16;
 }
 
+// A lane's code words as fp16 pairs (1024 + code, or 1024 + 2^(b pos) code
+// at the higher positions), decoded once and dotted with several tokens.
+template <int BITS, int V>
+__device__ __forceinline__ void decode_words(const uint32_t (&cw)[V],
+                                             uint32_t (&d)[V][QT<BITS>::PPW]) {
+  constexpr int NPOS = QT<BITS>::NPOS;
+#pragma unroll
+  for (int w = 0; w < V; ++w)
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      const uint32_t v = hs ? (cw[w] >> 8) : cw[w];
+#pragma unroll
+      for (int pos = 0; pos < NPOS; ++pos) {
+        constexpr uint32_t base = (1u << BITS) - 1u;
+        const uint32_t m = (base << (BITS * pos)) | (base << (BITS * pos + 16));
+        d[w][hs * NPOS + pos] = and_or(v, m, 0x64006400u);
+      }
+    }
+}
+
+// lane_row over decoded words: sum over the lane's words of
+// scale(word) * (dot - K), for one row (K folded).
+template <int BITS, int V, bool SPLIT>
+__device__ __forceinline__ float lane_row_dec(const uint32_t (&d)[V][QT<BITS>::PPW],
+                                              const XRegs<BITS, V, SPLIT>& X,
+                                              const float (&s)[ScalePlan<BITS, V>::NS],
+                                              int tmask) {
+  using SP = ScalePlan<BITS, V>;
+  constexpr int PPW = QT<BITS>::PPW;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < SP::N4; ++c) {
+    float a = -X.K[c];
+#pragma unroll
+    for (int w = 4 * c; w < 4 * c + 4; ++w)
+#pragma unroll
+      for (int q = 0; q < PPW; ++q) {
+        a = fdot2(d[w][q], X.hi[w][q], a);
+        if constexpr (SPLIT) a = fdot2(d[w][q], X.lo[w][q], a);
+      }
+    acc = fmaf(a, s[c], acc);
+  }
+  if constexpr (SP::R > 0) {
+    // the tail's scale(s) as opaque register values, so the per-word choice
+    // stays a register select (not an indexed load from a stack copy)
+    float t0 = s[SP::N4], t1 = s[SP::NS - 1];
+    asm volatile("" : "+v"(t0), "+v"(t1));
+#pragma unroll
+    for (int t = 0; t < SP::R; ++t) {
+      const int w = 4 * SP::N4 + t;
+      float a = -X.K[SP::N4 + t];
+#pragma unroll
+      for (int q = 0; q < PPW; ++q) {
+        a = fdot2(d[w][q], X.hi[w][q], a);
+        if constexpr (SPLIT) a = fdot2(d[w][q], X.lo[w][q], a);
+      }
+      const float sc = (SP::NT == 2 && ((tmask >> t) & 1)) ? t1 : t0;
+      acc = fmaf(a, sc, acc);
+    }
+  }
+  return acc;
+}
+
 // tokens per wave when building the activation pairs (wave w takes w, w + 8, ...)
 constexpr int SB_XSLOTS = (SB_TMAX + DEC_WAVES - 1) / DEC_WAVES;
 
@@ -386,13 +449,27 @@ k_sb_gate_up(SmallArgs A) {
       // make the compiler wait for every outstanding load (the next batch
       // included) before the loop
       int rank = 0;
+      // the row's words decoded once for all of its tokens (with two waves
+      // per SIMD; at four the registers do not hold them)
+      constexpr bool DEC1 = !sb_narrow<BITS, VG, XF32>();
+      uint32_t dg[DEC1 ? VG : 1][PPW], du[DEC1 ? VG : 1][PPW];
+      if constexpr (DEC1) {
+        decode_words<BITS, VG>(B.gw[i], dg);
+        decode_words<BITS, VG>(B.uw[i], du);
+      }
       while (m) {
         const int t = __builtin_ctz(m);
         m &= m - 1u;
         XRegs<BITS, VG, SPLIT> X;
         load_x(t, X);
-        float ag = lane_row<BITS, VG, SPLIT>(B.gw[i], X, B.gs[i], tmg);
-        float au = lane_row<BITS, VG, SPLIT>(B.uw[i], X, B.us[i], tmg);
+        float ag, au;
+        if constexpr (DEC1) {
+          ag = lane_row_dec<BITS, VG, SPLIT>(dg, X, B.gs[i], tmg);
+          au = lane_row_dec<BITS, VG, SPLIT>(du, X, B.us[i], tmg);
+        } else {
+          ag = lane_row<BITS, VG, SPLIT>(B.gw[i], X, B.gs[i], tmg);
+          au = lane_row<BITS, VG, SPLIT>(B.uw[i], X, B.us[i], tmg);
+        }
         ag = seg_sum(ag, lgg);
         au = seg_sum(au, lgg);
         if (lrg == LPRG - 1) {
