@@ -236,8 +236,11 @@ def main():
             if name == "gate_up":
                 byts = [ui * gu_raw + sh_gu + x_bytes + T * E * 4 + h_bytes for ui in u]
             else:
+                # the grouped down stage writes one row per pair for the
+                # combine; the one-token and 1-4-token stages write out
+                y_b = out_b if T <= 4 else (T * k + nsh * T) * W.d_model * 4
                 byts = [ui * dn_raw + h_bytes + out_b if single else
-                        ui * dn_raw + sh_dn + h_bytes + (T * k + nsh * T) * W.d_model * 4
+                        ui * dn_raw + sh_dn + h_bytes + y_b
                         for ui in u]
             mean_dt = sum(dts) / n
             mean_b = sum(byts) / n
@@ -247,6 +250,9 @@ def main():
     if single:
         names = {"gate_up": "k_dec_gate_up (routing + gate/up + SwiGLU)",
                  "down": "k_dec_down (down projection + weighted combine)"}
+    elif T <= 4:
+        names = {"gate_up": "k_sb_gate_up (routing + grouping + gate/up + SwiGLU)",
+                 "down": "k_sb_down (down projection + weighted combine)"}
     else:
         names = {"gate_up": "k_gate_up (grouped gate/up + SwiGLU over the routed pairs)",
                  "down": "k_down (grouped down projection)"}

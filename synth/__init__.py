@@ -73,6 +73,12 @@ WORKLOADS = {
     # DeepSeek-MoE-16B-shaped layer, 8 tokens, plus an always-on shared expert
     "deepseek16b_q4_b8": Workload("deepseek16b_q4_b8", 2048, 1408, 64, 6, 8, 4, False,
                                   shared_ffn_dim=2816, seed=4),
+    # small decode batches of the same two layers (1-4 tokens)
+    "qwen235b_q4_b4": Workload("qwen235b_q4_b4", 4096, 1536, 128, 8, 4, 4, True, seed=8),
+    "deepseek16b_q4_b1": Workload("deepseek16b_q4_b1", 2048, 1408, 64, 6, 1, 4, False,
+                                  shared_ffn_dim=2816, seed=9),
+    "deepseek16b_q4_b4": Workload("deepseek16b_q4_b4", 2048, 1408, 64, 6, 4, 4, False,
+                                  shared_ffn_dim=2816, seed=10),
     # the same layer at prefill-sized batches (matrix-core grouped stages)
     "qwen235b_q4_t512": Workload("qwen235b_q4_t512", 4096, 1536, 128, 8, 512, 4, True,
                                  seed=6),
