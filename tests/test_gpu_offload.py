@@ -66,7 +66,9 @@ class Offloaded:
 
 
 @pytest.mark.parametrize("T,slots,shared", [(1, 0, 0), (1, 4, 0), (6, 0, 0), (6, 5, 256),
-                                            (1, 16, 0), (6, 1, 0)])
+                                            (1, 16, 0), (6, 1, 0),
+                                            # the 1-4-token launches through the table
+                                            (3, 0, 256), (4, 2, 0), (1, 0, 512)])
 def test_offload_equals_device_forward_and_oracle(T, slots, shared):
     _torch()
     d, ffn, E, k = 512, 256, 16, 4
