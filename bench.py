@@ -257,7 +257,8 @@ def main():
         names = {"gate_up": "k_gate_up (grouped gate/up + SwiGLU over the routed pairs)",
                  "down": "k_down (grouped down projection)"}
     dom = kern.get("gate_up")
-    traffic = committed_traffic(W.name, "gate_up" if single else "gate_up_grouped")
+    traffic = committed_traffic(W.name, "gate_up" if single else
+                                ("gate_up_small" if T <= 4 else "gate_up_grouped"))
     # the gate/up launch's contraction: two flops per weight per routed pair
     # (one layer per launch); the roofline is whichever peak bounds it first
     gu_flops = (T * k + nsh * T) * 4 * W.d_model * W.ffn_dim
@@ -577,6 +578,8 @@ def bench_offload(args):
 
 KERNEL_SOURCES = {
     "gate_up": ("smoe_decode.hpp", "smoe_decode_args.hpp", "smoe_device.hpp"),
+    "gate_up_small": ("smoe_small.hpp", "smoe_small_args.hpp", "smoe_decode.hpp",
+                      "smoe_decode_args.hpp", "smoe_device.hpp"),
     "gate_up_grouped": ("smoe_gemm.hpp", "smoe_gemv_args.hpp", "smoe_device.hpp"),
 }
 
