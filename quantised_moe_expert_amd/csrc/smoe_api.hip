@@ -270,7 +270,14 @@ int forward_impl(const LayerInfo& L, const void* x, int xmode, float eps, const 
     if (side_ok && (rc = check_hip(hipEventRecord(L.join, L.side), "shared-expert join")))
       return rc;
   }
-  if ((rc = check_hip(launch_route(logits, T, E, k, norm, ids, w, uids, uw, 1, meta, active,
+  bool routed = false;
+  if (cfg.is_default() && !gmk_wanted(pairs, max_slots) &&
+      (rc = check_hip(small_route_try(L, logits, T, k, norm, nsh, uids, uw, ids, w, meta, active,
+                                      offs, pair_token, pair_of, s, &routed),
+                      "small-batch route launch")))
+    return rc;
+  if (!routed &&
+      (rc = check_hip(launch_route(logits, T, E, k, norm, ids, w, uids, uw, 1, meta, active,
                                    offs, pair_token, pair_of, s, cfg, nsh),
                       "route launch")))
     return rc;

@@ -270,6 +270,53 @@ hipError_t small_try(const LayerInfo& L, const void* x, bool xf32, bool rms, flo
   return hipSuccess;
 }
 
+hipError_t small_route_try(const LayerInfo& L, const float* logits, int T, int k, int norm,
+                           int nsh, int32_t* uids, float* uw, int32_t* ids, float* w, int* meta,
+                           int* active, int* offs, int* pair_token, int* pair_of,
+                           hipStream_t stream, bool* launched) {
+  *launched = false;
+  const ExpertPlan& P = L.plan;
+  const int E = (int)L.desc.num_experts, bits = (int)L.desc.bits;
+  // one workgroup ranks T x E keys: past 1024 of them the top-k and grouping
+  // launches (spread over many workgroups) measured faster
+  if (T < 1 || T > SB_TSLOTS || (int64_t)T * E > 1024) return hipSuccess;
+  if (L.desc.shared_ffn_dim && nsh <= 0) return hipSuccess;
+  SbLaunch sb;
+  // any instantiation of the kernel serves (the gate/up part is not run)
+  if (!find_sb_any(bits, (int)L.desc.scale_dtype, P.gate.v, false, &sb)) return hipSuccess;
+  SmallArgs A{};
+  A.lds_lv = (int)align16((uint64_t)T * E * 8);
+  A.lds_xp = (int)align16(A.lds_lv + (uint64_t)T * E * 4);
+  A.lds_k = A.lds_xp;
+  A.lds_os = A.lds_xp;
+  A.lds_total = A.lds_xp;
+  A.route_only = 1;
+  A.blobs = L.blobs;
+  A.stride = L.desc.blob_stride;
+  A.d = P.d_model;
+  A.ffn = P.ffn;
+  A.E = E;
+  A.k = k;
+  A.T = T;
+  A.norm = norm;
+  A.nsh = nsh;
+  A.lg_g = P.gate.lpr_log2;
+  A.logits = logits;
+  A.ids = ids;
+  A.w = w;
+  A.meta = meta;
+  A.active = active;
+  A.offs = offs;
+  A.pair_token = pair_token;
+  A.pair_of = pair_of;
+  A.user_ids = uids;
+  A.user_w = uw;
+  const hipError_t e = sb(A, 1, stream);
+  if (e != hipSuccess) return e;
+  *launched = true;
+  return hipSuccess;
+}
+
 hipError_t small_down_try(const LayerInfo& L, const float* h, int T, int k, int nsh,
                           const int* meta, const int* active, const int* offs,
                           const int* pair_token, const int* pair_of, const float* w, float* out,

@@ -142,6 +142,15 @@ hipError_t small_try(const LayerInfo& L, const void* x, bool xf32, bool rms, flo
                      int* pair_token, int* pair_of, float* h, hipStream_t stream,
                      bool* launched);
 
+// Up to 16 tokens: routing and grouping in one single-workgroup launch (the
+// first part of the small-batch gate/up kernel), writing ids, w, meta,
+// active, offs, pair_token and pair_of as the grouping launch does. Sets
+// *launched = false, enqueuing nothing, when the shape does not fit.
+hipError_t small_route_try(const LayerInfo& L, const float* logits, int T, int k, int norm,
+                           int nsh, int32_t* uids, float* uw, int32_t* ids, float* w, int* meta,
+                           int* active, int* offs, int* pair_token, int* pair_of,
+                           hipStream_t stream, bool* launched);
+
 // Small batches (1..16 tokens) in the grouped layout: the down stage of every
 // grouped pair and the weighted combine (out = or += sum_j w[t, j] y[pair] +
 // the shared expert's parts) in one launch. Sets *launched = false, enqueuing

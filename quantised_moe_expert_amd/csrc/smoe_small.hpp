@@ -195,6 +195,45 @@ k_sb_gate_up(SmallArgs A) {
   }
   __syncthreads();
   const int nact = s_nact;
+  // the selection, the weights and the grouped layout, published by
+  // workgroup 0 (wave w takes token w)
+  auto publish = [&]() {
+    for (int t = wave; t < T; t += DEC_WAVES) {
+      const float mx = s_val[t * k];
+      float se = 0.f;
+      for (int e = lane; e < E; e += 64) se += expf(s_lv[t * E + e] - mx);
+      se = lane63(seg_sum(se, 6));
+      const float p = lane < k ? expf(s_val[t * k + (lane < k ? lane : 0)] - mx) / se : 0.f;
+      const float psum = lane63(seg_sum(p, 6));
+      if (lane < k) {
+        const int e = s_sel[t * k + lane];
+        const float wt = A.norm ? p / psum : p;
+        const int o = t * k + lane;
+        const int pos = s_off[s_slot[e]] + __popc(s_mask[e] & ((1u << t) - 1u));
+        A.ids[o] = e;
+        A.w[o] = wt;
+        A.pair_of[o] = pos;
+        A.pair_token[pos] = t;
+        if (A.user_ids) A.user_ids[o] = e;
+        if (A.user_w) A.user_w[o] = wt;
+      }
+    }
+    for (int s = tid; s < nact; s += DEC_THREADS) {
+      A.active[s] = s_act[s];
+      A.offs[s] = s_off[s];
+    }
+    for (int v = tid; v <= nsh; v += DEC_THREADS) A.offs[nact + v] = P + v * T;
+    for (int i = tid; i < nsh * T; i += DEC_THREADS) A.pair_token[P + i] = i % T;
+    if (tid == 0) {
+      A.meta[0] = nact;
+      A.meta[1] = P;
+    }
+  };
+  // routing and grouping only (one workgroup, ahead of the grouped stages)
+  if (A.route_only) {
+    publish();
+    return;
+  }
 
   // 4. this wave's units: (slot, row group) over the shared expert's parts
   //    first (all T tokens each), then the active experts, split evenly over
@@ -295,39 +334,8 @@ k_sb_gate_up(SmallArgs A) {
   issue_b(bA, 0);
 
   // 5. workgroup 0 publishes the selection, the weights and the grouped
-  //    layout; wave w takes token w
-  if (blockIdx.x == 0) {
-    for (int t = wave; t < T; t += DEC_WAVES) {
-      const float mx = s_val[t * k];
-      float se = 0.f;
-      for (int e = lane; e < E; e += 64) se += expf(s_lv[t * E + e] - mx);
-      se = lane63(seg_sum(se, 6));
-      const float p = lane < k ? expf(s_val[t * k + (lane < k ? lane : 0)] - mx) / se : 0.f;
-      const float psum = lane63(seg_sum(p, 6));
-      if (lane < k) {
-        const int e = s_sel[t * k + lane];
-        const float wt = A.norm ? p / psum : p;
-        const int o = t * k + lane;
-        const int pos = s_off[s_slot[e]] + __popc(s_mask[e] & ((1u << t) - 1u));
-        A.ids[o] = e;
-        A.w[o] = wt;
-        A.pair_of[o] = pos;
-        A.pair_token[pos] = t;
-        if (A.user_ids) A.user_ids[o] = e;
-        if (A.user_w) A.user_w[o] = wt;
-      }
-    }
-    for (int s = tid; s < nact; s += DEC_THREADS) {
-      A.active[s] = s_act[s];
-      A.offs[s] = s_off[s];
-    }
-    for (int v = tid; v <= nsh; v += DEC_THREADS) A.offs[nact + v] = P + v * T;
-    for (int i = tid; i < nsh * T; i += DEC_THREADS) A.pair_token[P + i] = i % T;
-    if (tid == 0) {
-      A.meta[0] = nact;
-      A.meta[1] = P;
-    }
-  }
+  //    layout
+  if (blockIdx.x == 0) publish();
 
   // 6. fp16 activation pairs and offsets K of every token, built once per
   //    workgroup in LDS from the words loaded in step 4 (wave w takes token w)
@@ -496,7 +504,7 @@ k_sb_gate_up(SmallArgs A) {
 // (reduced to DEC_NWG for the instantiations built for one)
 template <int BITS, typename ST, int VG, bool XF32>
 hipError_t launch_sb_gate_up(const SmallArgs& A, int nwg, hipStream_t s) {
-  if (!sb_narrow<BITS, VG, XF32>()) nwg = DEC_NWG;
+  if (!sb_narrow<BITS, VG, XF32>() && !A.route_only) nwg = DEC_NWG;
   auto kernel = k_sb_gate_up<BITS, ST, VG, XF32>;
   if (A.lds_total > 65536) {  // workgroups of more than 64 KB of LDS need the limit raised
     const hipError_t e = hipFuncSetAttribute(

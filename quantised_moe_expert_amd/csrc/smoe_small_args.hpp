@@ -41,6 +41,7 @@ struct SmallArgs {
   float* user_w;         // optional [T * k]
   // dynamic LDS layout (bytes)
   int lds_lv, lds_xp, lds_k, lds_os, lds_total;
+  int route_only;        // one workgroup: routing, grouping and the layout only
 };
 
 template <int BITS, typename ST, int VG, bool XF32>
